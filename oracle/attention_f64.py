@@ -1,0 +1,241 @@
+"""Float64 CPU oracle for exact attention: plain, slow, obviously correct.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The GPU library never calls it, and
+this module imports nothing from the GPU library.
+
+What is computed follows the pages' own statement of the problem:
+
+* "FlashAttention and efficient attention kernels" (plumephp tutorial),
+  section "Standard attention" (three steps S = Q Kᵀ, P = softmax(S), O = P V)
+  and the concept page "Flash-Attention" (awesome-system-papers), section
+  "Core idea", which writes the scaled form softmax(Q Kᵀ/√d) V and states that
+  the tiled method is mathematically equal to it.  The oracle is therefore the
+  three-step definition itself, in float64, one (batch, head) at a time.
+* Backward: the tutorial's sections "Backward" and "Backward recompute flow"
+  say only that dQ/dK/dV are obtained from Q, K, V, the saved statistics and
+  dO.  The pages print no gradient formula, so the oracle uses the plain chain
+  rule of the three-step definition (pinned by finite differences and by
+  torch's CPU float64 autograd in the tests).
+* Streaming normaliser: the tutorial's sections "Online softmax",
+  "Correction formula" and the worked example ("streaming process"), and the
+  related-work page's paper #1 (Online normalizer calculation for softmax).
+* Decode over a paged KV cache: the tutorial's "Variant family" section
+  (FlashDecoding splits the KV sequence; PagedAttention reads non-contiguous
+  fixed-size blocks) and the related-work page's paper #5 (PagedAttention).
+  The oracle gathers the pages back into a contiguous sequence and applies the
+  three-step definition with one query row.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes):
+* scale is an explicit argument applied to S before the mask and the max;
+* causal masking is bottom-right aligned: key j is visible to query i iff
+  j <= i + (Nk - Nq);
+* a row with no visible key has O = 0, LSE = -inf and zero gradients;
+* grouped-query heads are contiguous groups: kv head = q head // (Hq / Hkv);
+* LSE = m + ln(l) in natural log;
+* KV cache pages are laid out [num_blocks, Hkv, block_size, d].
+
+Every function here is pinned in ``tests/test_oracle.py`` against values and
+properties that the pages and the mathematics fix.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "visible_mask",
+    "attention_probs",
+    "attention_fwd",
+    "attention_bwd",
+    "decode_paged",
+    "gather_pages",
+    "online_softmax_stats",
+    "merge_softmax_stats",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def visible_mask(nq: int, nk: int, causal: bool, row_ids=None, nq_total=None) -> np.ndarray:
+    """Boolean [nq, nk] mask of the (query, key) pairs that take part.
+
+    Causal alignment is bottom-right: query row i of a query sequence of
+    length ``nq_total`` sees key j iff ``j <= i + (nk - nq_total)``.  To
+    evaluate a subset of rows of a longer query sequence, pass their indices
+    in ``row_ids`` and the full length in ``nq_total`` (defaults: all rows,
+    ``nq_total = nq``).
+    """
+    if not causal:
+        return np.ones((nq, nk), dtype=bool)
+    rows = np.arange(nq) if row_ids is None else np.asarray(row_ids, dtype=np.int64)
+    total = nq if nq_total is None else int(nq_total)
+    return np.arange(nk)[None, :] <= (rows + (nk - total))[:, None]
+
+
+def attention_probs(q, k, scale: float, causal: bool, row_ids=None, nq_total=None):
+    """P = softmax(scale * q kᵀ) row-wise, with masked entries exactly 0.
+
+    q: [Nq, d], k: [Nk, d].  Returns (P [Nq, Nk], LSE [Nq]).  A row with no
+    visible key returns P = 0 and LSE = -inf.  ``row_ids``/``nq_total`` select
+    the causal horizon of a subset of rows (see ``visible_mask``).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    s = scale * (q @ k.T)
+    vis = visible_mask(q.shape[0], k.shape[0], causal, row_ids, nq_total)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 on masked entries
+    l = e.sum(axis=1)
+    p = np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, l)[:, None])
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return p, lse
+
+
+def _check_heads(hq: int, hkv: int) -> int:
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"Hq={hq} must be a positive multiple of Hkv={hkv}")
+    return hq // hkv
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool, row_ids=None, nq_total=None):
+    """Exact attention forward.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d].  Returns O [B, Hq, Nq, d] and
+    LSE [B, Hq, Nq] in float64.  Query head h reads kv head h // (Hq/Hkv).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    bsz, hq, nq, d = q.shape
+    hkv = k.shape[1]
+    g = _check_heads(hq, hkv)
+    o = np.zeros((bsz, hq, nq, v.shape[3]))
+    lse = np.zeros((bsz, hq, nq))
+    for b in range(bsz):
+        for h in range(hq):
+            p, lse[b, h] = attention_probs(q[b, h], k[b, h // g], scale, causal, row_ids, nq_total)
+            o[b, h] = p @ v[b, h // g]
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool, row_ids=None, nq_total=None):
+    """Gradients of sum(O * dO) with respect to Q, K and V.
+
+    Plain chain rule through the three-step definition:
+        O  = P V,  P = softmax(S) row-wise,  S = scale * Q Kᵀ (masked)
+        dV = Pᵀ dO
+        dP = dO Vᵀ
+        dS = P ∘ (dP − D 1ᵀ),  D_i = Σ_c dO_ic O_ic   (= Σ_j P_ij dP_ij)
+        dQ = scale · dS K,      dK = scale · dSᵀ Q
+    For grouped heads, dK and dV of a kv head are summed over its query heads.
+    Returns (dQ, dK, dV) in float64 with the shapes of q, k, v.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    bsz, hq, nq, d = q.shape
+    hkv = k.shape[1]
+    g = _check_heads(hq, hkv)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(bsz):
+        for h in range(hq):
+            kh, vh = k[b, h // g], v[b, h // g]
+            p, _ = attention_probs(q[b, h], kh, scale, causal, row_ids, nq_total)
+            o = p @ vh
+            dd = (do[b, h] * o).sum(axis=1)
+            dp = do[b, h] @ vh.T
+            ds = p * (dp - dd[:, None])
+            dq[b, h] = scale * (ds @ kh)
+            dk[b, h // g] += scale * (ds.T @ q[b, h])
+            dv[b, h // g] += p.T @ do[b, h]
+    return dq, dk, dv
+
+
+def gather_pages(cache, block_table_row, seq_len: int) -> np.ndarray:
+    """Contiguous [Hkv, seq_len, d] keys (or values) of one sequence.
+
+    cache: [num_blocks, Hkv, block_size, d]; token t lives in page
+    ``block_table_row[t // block_size]`` at slot ``t % block_size``.
+    """
+    cache = np.asarray(cache)
+    num_blocks, hkv, bs, d = cache.shape
+    out = np.zeros((hkv, seq_len, d), dtype=np.float64)
+    for t in range(0, seq_len, bs):
+        page = int(block_table_row[t // bs])
+        if not 0 <= page < num_blocks:
+            raise IndexError(f"block table entry {page} outside [0, {num_blocks})")
+        n = min(bs, seq_len - t)
+        out[:, t:t + n, :] = cache[page, :, :n, :]
+    return out
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
+    """One-token decode over a paged KV cache.
+
+    q: [B, Hq, d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d];
+    block_table: [B, max_blocks] integer page ids; seq_lens: [B] token counts.
+    The single query row sees every cached token of its sequence (it is the
+    last position), so no mask applies.  Returns O [B, Hq, d], LSE [B, Hq];
+    a sequence of length 0 gives O = 0 and LSE = -inf.
+    """
+    q = _f64(q)
+    bsz, hq, d = q.shape
+    hkv = np.asarray(k_cache).shape[1]
+    g = _check_heads(hq, hkv)
+    o = np.zeros((bsz, hq, d))
+    lse = np.zeros((bsz, hq))
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        kb = gather_pages(k_cache, block_table[b], n)
+        vb = gather_pages(v_cache, block_table[b], n)
+        for h in range(hq):
+            p, lse_row = attention_probs(q[b, h][None, :], kb[h // g], scale, False)
+            o[b, h] = (p @ vb[h // g])[0]
+            lse[b, h] = lse_row[0]
+    return o, lse
+
+
+def online_softmax_stats(x, block: int):
+    """Streaming (max, sum) of one row, visiting it ``block`` entries at a time.
+
+    This is the update of the tutorial's "Online softmax" and "Correction
+    formula" sections: on each new block the running max becomes
+    max(old max, block max), the old running sum is rescaled by
+    exp(old max − new max), and the block's exponentials, taken relative to the
+    new max, are added.  Returns (m, l) with softmax denominator
+    l = Σ exp(x − m).  An empty or all −inf row gives (−inf, 0).
+    """
+    x = _f64(x).ravel()
+    m, l = -math.inf, 0.0
+    for start in range(0, x.size, block):
+        blk = x[start:start + block]
+        m_new = max(m, float(blk.max()))
+        if m_new == -math.inf:
+            continue
+        rescale = 0.0 if m == -math.inf else math.exp(m - m_new)
+        l = l * rescale + float(np.exp(blk - m_new).sum())
+        m = m_new
+    return m, l
+
+
+def merge_softmax_stats(m_a: float, l_a: float, m_b: float, l_b: float):
+    """Combine two partial (max, sum) pairs taken over disjoint parts of a row.
+
+    Each part's sum is relative to its own max, so both are rescaled to the
+    common max:  M = max(m_a, m_b),  L = l_a·exp(m_a − M) + l_b·exp(m_b − M).
+    (When part b's max is already the common max this is the tutorial's
+    correction formula verbatim.)  Empty parts are (−inf, 0).
+    """
+    mx = max(m_a, m_b)
+    if mx == -math.inf:
+        return -math.inf, 0.0
+    wa = 0.0 if m_a == -math.inf else math.exp(m_a - mx)
+    wb = 0.0 if m_b == -math.inf else math.exp(m_b - mx)
+    return mx, l_a * wa + l_b * wb
