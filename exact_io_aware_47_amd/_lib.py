@@ -1,0 +1,187 @@
+"""ctypes binding of ``libflash_attn_mi355x.so`` (argument marshalling only).
+
+Every function here takes torch tensors, checks that they are dense device
+tensors of one supported dtype, allocates missing outputs with torch (device
+memory is torch's job), and passes raw pointers, sizes and torch's current HIP
+stream to the C ABI declared in ``include/flash_attn.h``.  All arithmetic runs
+in the library's HIP kernels; there is no other code path.  If the library is
+not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflash_attn_mi355x.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
+    5: "FA_ERR_GQA", 6: "FA_ERR_BLOCKSIZE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_SCALE",
+}
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+SIGNATURES = {
+    "flash_attn_strerror": (ctypes.c_char_p, [_i]),
+    "flash_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "flash_attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "flash_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_decode_num_splits": (_i, [_i, _i, _i, _i]),
+    "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({strerror(code)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_47_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().flash_attn_strerror(code).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise FlashAttnError(code, what)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dense(name: str, t: torch.Tensor, dtype=None, ndim=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return _DTYPE_CODE[t.dtype]
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, causal: bool = False, scale=None, out=None, lse=None):
+    """O, LSE = attention(q, k, v).  q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d]."""
+    _dense("q", q, ndim=4)
+    _dense("k", k, q.dtype, 4)
+    _dense("v", v, q.dtype, 4)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _dense("lse", lse, torch.float32)
+    code = lib().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                _default_scale(d, scale), int(bool(causal)), _dtype_code(q), _stream(q.device))
+    _check(code, "flash_attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype_code) -> int:
+    return int(lib().flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype_code))
+
+
+def bwd(q, k, v, out, dout, lse, causal: bool = False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of sum(O * dO) given the forward's O and LSE."""
+    _dense("q", q, ndim=4)
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _dense(name, t, q.dtype, 4)
+    _dense("lse", lse, torch.float32, 3)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q) if dq is None else _dense("dq", dq, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _dense("dk", dk, q.dtype)
+    dv = torch.empty_like(v) if dv is None else _dense("dv", dv, q.dtype)
+    code_dt = _dtype_code(q)
+    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, code_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    code = lib().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, Hq, Hkv, Nq, Nk, d, _default_scale(d, scale), int(bool(causal)), code_dt,
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def decode_num_splits(B, Hkv, max_blocks_per_seq, block_size=16) -> int:
+    return int(lib().flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size))
+
+
+def decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size=16, num_splits=0) -> int:
+    return int(lib().flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, num_splits))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_splits: int = 0, out=None, lse=None,
+                 workspace=None, want_lse: bool = True):
+    """One-token split-KV decode over a paged cache.  q [B,Hq,d];
+    k_cache, v_cache [num_blocks,Hkv,block_size,d]; block_table [B,max_blocks]
+    int32; seq_lens [B] int32."""
+    _dense("q", q, ndim=3)
+    _dense("k_cache", k_cache, q.dtype, 4)
+    _dense("v_cache", v_cache, q.dtype, 4)
+    _dense("block_table", block_table, torch.int32, 2)
+    _dense("seq_lens", seq_lens, torch.int32, 1)
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dense("lse", lse, torch.float32)
+    ws_bytes = decode_workspace_bytes(B, Hq, Hkv, d, max_blocks, bs, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    code = lib().flash_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                         _ptr(out), _ptr(lse), B, Hq, Hkv, d, bs, max_blocks, num_blocks,
+                                         _default_scale(d, scale), int(num_splits), _dtype_code(q),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(q.device))
+    _check(code, "flash_attn_decode_paged")
+    return out, lse

@@ -1,0 +1,134 @@
+// fa_api.cpp -- C ABI of the attention library: argument validation (host
+// only, before any HIP call), workspace sizing and kernel dispatch.
+#include "flash_attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per tensor, keeps 32-bit element offsets valid
+constexpr int kCUs = 256;                        // MI355X compute units (sizes the automatic split count)
+
+int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+bool dtype_ok(int dtype) { return dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16; }
+bool headdim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Shared checks of the dense entry points, in the documented order.
+int check_dense(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int dtype) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (!headdim_ok(d)) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if ((int64_t)B * Hq * Nq * d >= kMaxElems || (int64_t)B * Hkv * Nk * d >= kMaxElems) return FA_ERR_SHAPE;
+  // One (batch, head) slab is addressed with 32-bit byte offsets.
+  if ((int64_t)Nq * d * elem_bytes(dtype) >= kMaxElems || (int64_t)Nk * d * elem_bytes(dtype) >= kMaxElems)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* flash_attn_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid size (non-positive, or tensor too large)";
+    case FA_ERR_HEADDIM: return "head dimension must be 32, 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_F32, FA_F16 or FA_BF16";
+    case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case FA_ERR_BLOCKSIZE: return "KV cache page size must be 16 tokens";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCALE: return "scale must be finite";
+  }
+  return "unknown error code";
+}
+
+int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  const int st = check_dense(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
+size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype) {
+  if (check_dense(B, Hq, Hkv, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
+  return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                   void* dQ, void* dK, void* dV, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                   int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+  const int st = check_dense(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype))
+    return FA_ERR_WORKSPACE;
+  fa::BwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
+  a.dq = dQ; a.dk = dK; a.dv = dV; a.dsum = (float*)workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  return launch_status(fa::launch_bwd(a, (hipStream_t)stream));
+}
+
+int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {
+  if (B <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || block_size != 16) return 0;
+  // Aim for 4 work-groups per compute unit, with at least 4 pages per split.
+  const int64_t units = (int64_t)B * Hkv;
+  int64_t splits = (4 * kCUs + units - 1) / units;
+  const int64_t max_splits = max_blocks_per_seq / 4 > 0 ? max_blocks_per_seq / 4 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  return (int)splits;
+}
+
+size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq, int block_size,
+                                         int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !headdim_ok(d) || max_blocks_per_seq <= 0 ||
+      block_size != 16 || num_splits < 0)
+    return 0;
+  const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
+  return (size_t)B * Hq * splits * (d + 2) * sizeof(float);
+}
+
+int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                            const int* seq_lens, void* O, float* LSE, int B, int Hq, int Hkv, int d, int block_size,
+                            int max_blocks_per_seq, int num_blocks, float scale, int num_splits, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !O) return FA_ERR_NULL;
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_splits < 0)
+    return FA_ERR_SHAPE;
+  if (!headdim_ok(d)) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if (block_size != 16) return FA_ERR_BLOCKSIZE;
+  if ((int64_t)num_blocks * Hkv * block_size * d >= kMaxElems || (int64_t)B * max_blocks_per_seq >= kMaxElems)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
+  if (!workspace ||
+      workspace_bytes < flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, splits))
+    return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a;
+  a.q = Q; a.k_cache = K_cache; a.v_cache = V_cache; a.block_table = block_table; a.seq_lens = seq_lens;
+  a.o = O; a.lse = LSE; a.part = (float*)workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.block_size = block_size; a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks; a.splits = splits; a.scale = scale; a.dtype = dtype;
+  return launch_status(fa::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,280 @@
+// fa_device.hpp -- gfx950 device building blocks shared by the attention kernels.
+//
+// Matrix-core fragments (CDNA4 MFMA, wave64), bounds-checked buffer loads
+// (direct to LDS or to registers), the swizzled LDS tile addressing, the
+// transposing LDS read, and the float32 <-> 16-bit conversions.
+//
+// MFMA layouts used throughout (v_mfma_f32_32x32x16_{bf16,f16} and the
+// float32 v_mfma_f32_32x32x2f32), with lane l and half h = l / 32:
+//   A (32 x 16, M x K): lane l holds row l % 32, k = 8h .. 8h+7
+//   B (16 x 32, K x N): lane l holds column l % 32, k = 8h .. 8h+7
+//   C (32 x 32)       : lane l, register r holds column l % 32 and
+//                       row 8*(r/4) + 4h + (r%4)
+// For float32 a 16-wide k block is eight 32x32x2 products; product t takes
+// slot t of each half, so lane half h still supplies k = 8h + t.  Which k a
+// slot stands for never matters for a contraction as long as A and B agree.
+//
+// Row permutation sigma: if the A rows fed to an MFMA are permuted by sigma
+// (swap bits 2 and 3 of the row index), the C register r of lane half h holds
+// row 16*(r/8) + 8h + (r%8).  Registers 0..7 (and 8..15) then form exactly the
+// B-operand layout of a following product that contracts over those rows, so
+// P = softmax(S) can feed the next MFMA straight from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Reinterpret a 32-bit word as float.  Takes the word by value: bit-casting a
+// vector element expression in place (v[i]) reads element 0 with this
+// compiler, so element accesses always go through this function.
+__device__ __forceinline__ float as_float(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / 64); }
+
+// --------------------------------------------------------------------------
+// Element types.  Frag<T>: one lane's 8 consecutive k values of an A or B
+// operand for a 16-wide k block.
+// --------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+  typedef bf16x8 Frag;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ f32x16 mma(const Frag& a, const Frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Frag pack(const float* x) {
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) f[i] = (__bf16)x[i];  // v_cvt_pk_bf16_f32, round to nearest even
+    return f;
+  }
+  __device__ static __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+};
+
+template <> struct Elem<_Float16> {
+  typedef f16x8 Frag;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ f32x16 mma(const Frag& a, const Frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Frag pack(const float* x) {
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) f[i] = (_Float16)x[i];  // round to nearest even
+    return f;
+  }
+  __device__ static __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+};
+
+struct F32Frag { float v[8]; };
+
+template <> struct Elem<float> {
+  typedef F32Frag Frag;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ f32x16 mma(const Frag& a, const Frag& b, f32x16 c) {
+#pragma unroll
+    for (int t = 0; t < 8; t++) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[t], b.v[t], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static __forceinline__ Frag pack(const float* x) {
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) f.v[i] = x[i];
+    return f;
+  }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+};
+
+// --------------------------------------------------------------------------
+// Buffer resources: raw (stride 0) descriptors whose byte range is checked by
+// the hardware.  Loads beyond num_bytes return zero, stores beyond it are
+// dropped, so ragged tails need no per-lane branches.
+// --------------------------------------------------------------------------
+constexpr int kBufferFlags = 0x00020000;  // gfx9 word 3: 32-bit data format, raw addressing
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L of the wave
+// writes lds_wave_base + 16 * L (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// --------------------------------------------------------------------------
+// LDS tiles: rows of ROW_BYTES, stored as 16-byte chunks whose position in a
+// row is XOR-permuted by a per-row key so that the access patterns of the
+// kernels hit distinct banks.
+//   TR = false: 16 consecutive rows at one chunk column hit 16 distinct
+//               16-byte bank groups (row-fragment reads).
+//   TR = true : 4 consecutive rows at an aligned group of 4 chunk columns hit
+//               distinct bank groups (transposing column-fragment reads).
+// --------------------------------------------------------------------------
+template <int ROW_BYTES, bool TR>
+struct Tile {
+  static constexpr int kChunks = ROW_BYTES / 16;                       // chunks per row
+  static constexpr int kRowsPerSweep = kChunks >= 16 ? 1 : 16 / kChunks;  // rows per 256 B
+  static constexpr int kKeyMask = (kChunks >= 16 ? 16 : kChunks) - 1;
+  __device__ static __forceinline__ int key(int row) {
+    if constexpr (!TR) {
+      return (row / kRowsPerSweep) & kKeyMask;
+    } else {
+      if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+      else if constexpr (kChunks == 8) return ((row >> 1) & 1) << 2;
+      else return 0;
+    }
+  }
+  // byte offset of logical chunk c of row `row`
+  __device__ static __forceinline__ uint32_t off(int row, int c) {
+    return (uint32_t)(row * ROW_BYTES + ((c ^ key(row)) << 4));
+  }
+};
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_char* base, uint32_t off) {
+  return *(const __attribute__((address_space(3))) u32x4*)(base + off);
+}
+__device__ __forceinline__ float lds_read_f32(const lds_char* base, uint32_t off) {
+  return *(const __attribute__((address_space(3))) float*)(base + off);
+}
+// Transposing read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// j supplies the address of 4 consecutive 16-bit elements (row j/4 of a 4-row
+// block, columns 4*(j%4)..+3); lane i receives column i of that 4 x 16 block,
+// i.e. the 4 elements (row 0..3, column i).
+__device__ __forceinline__ i16x4 lds_read_tr16(const lds_char* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + off));
+}
+
+// sigma: swap bits 2 and 3 of a row index within a 32-row MFMA tile.
+__device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// --------------------------------------------------------------------------
+// Cross-lane helpers
+// --------------------------------------------------------------------------
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// --------------------------------------------------------------------------
+// Operand fragments
+// --------------------------------------------------------------------------
+template <typename T>
+struct Frags {
+  typedef typename Elem<T>::Frag Frag;
+  static constexpr int kES = Elem<T>::kBytes;
+
+  // Row fragment from a swizzled LDS tile: elements 16*ks + 8h .. +7 of `row`
+  // (A operand with rows = tile rows, k = tile columns).
+  template <typename TileT>
+  __device__ static __forceinline__ Frag lds_row(const lds_char* base, int row, int ks, int h) {
+    if constexpr (kES == 2) {
+      return __builtin_bit_cast(Frag, lds_read16(base, TileT::off(row, 2 * ks + h)));
+    } else {
+      u32x4 a = lds_read16(base, TileT::off(row, 4 * ks + 2 * h));
+      u32x4 b = lds_read16(base, TileT::off(row, 4 * ks + 2 * h + 1));
+      Frag f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) { f.v[i] = as_float(a[i]); f.v[4 + i] = as_float(b[i]); }
+      return f;
+    }
+  }
+
+  // Column fragment from a swizzled LDS tile: rows r0 + 8h + t (t = 0..7) of
+  // column c0 + (lane % 32)  (A operand of the transposed tile: rows = tile
+  // columns, k = tile rows).  16-bit types use two transposing reads.
+  template <typename TileT>
+  __device__ static __forceinline__ Frag lds_col(const lds_char* base, int r0, int c0, int lane) {
+    const int h = lane >> 5;
+    if constexpr (kES == 2) {
+      const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      i16x4 t[2];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int row = r0 + 8 * h + 4 * u + ((lane & 15) >> 2);
+        t[u] = lds_read_tr16(base, TileT::off(row, col >> 3) + ((col & 7) << 1));
+      }
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      i16x8 c = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
+      return __builtin_bit_cast(Frag, c);
+    } else {
+      const int col = c0 + (lane & 31);
+      Frag f;
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const int row = r0 + 8 * h + t;
+        f.v[t] = lds_read_f32(base, TileT::off(row, col >> 2) + ((col & 3) << 2));
+      }
+      return f;
+    }
+  }
+
+  // Row fragment straight from a global [rows][D] slab (bounds-checked: rows
+  // past the resource's range read as zero).
+  template <int D>
+  __device__ static __forceinline__ Frag global_row(__amdgpu_buffer_rsrc_t r, int row, int ks, int h) {
+    const uint32_t off = (uint32_t)row * (D * kES) + (uint32_t)(16 * ks + 8 * h) * kES;
+    if constexpr (kES == 2) {
+      return __builtin_bit_cast(Frag, buf_load16(r, off));
+    } else {
+      u32x4 a = buf_load16(r, off), b = buf_load16(r, off + 16);
+      Frag f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) { f.v[i] = as_float(a[i]); f.v[4 + i] = as_float(b[i]); }
+      return f;
+    }
+  }
+
+  // Store 4 consecutive elements (rounded to T) at byte offset `off`.
+  __device__ static __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+    if constexpr (kES == 2) {
+      typedef T t2 __attribute__((ext_vector_type(2)));
+      t2 x = {(T)a, (T)b}, y = {(T)c, (T)d};
+      u32x2 w = {__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y)};
+      buf_store8(r, off, w);
+    } else {
+      u32x4 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                 __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+      buf_store16(r, off, w);
+    }
+  }
+};
+
+}  // namespace fa

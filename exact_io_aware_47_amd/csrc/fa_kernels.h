@@ -1,0 +1,56 @@
+// fa_kernels.h -- host-side launch interface of the attention kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  int dtype;  // enum fa_dtype
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic, [B, Hq, Nq] float32
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  int dtype;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int* block_table;
+  const int* seq_lens;
+  void* o;
+  float* lse;  // may be null
+  float* part; // workspace: [B, Hq, splits, d + 2] float32
+  int B, Hq, Hkv, d, block_size, max_blocks, num_blocks, splits;
+  float scale;
+  int dtype;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,165 @@
+/*
+ * flash_attn.h -- C ABI of the MI355X (gfx950) exact fused attention library.
+ *
+ * What is computed: exact attention O = softmax(scale * Q Kᵀ [+ causal mask]) V,
+ * tiled with an online softmax so that the N x N score matrix never reaches
+ * device memory, plus the recomputation backward and a split-KV decode over a
+ * paged KV cache.  Sources of each operation:
+ *
+ *   - Forward: "Flash-Attention" concept page (awesome-system-papers), section
+ *     "Core idea" (tiles of Q/K/V staged on chip; running max, running sum and
+ *     running output; Q outer, K/V inner as in FlashAttention-2) and the
+ *     tutorial "FlashAttention and efficient attention kernels" (plumephp),
+ *     sections "Standard attention", "Online softmax", "Correction formula",
+ *     "Forward" and the forward pseudocode skeleton.
+ *   - Backward: the same tutorial, sections "Backward" and "Backward recompute
+ *     flow" (S and P are rebuilt on chip from Q, K, V and the saved per-row
+ *     statistics, combined with dO into dQ, dK, dV, and discarded block by
+ *     block).
+ *   - Decode: the tutorial's "Variant family" section (FlashDecoding splits the
+ *     KV sequence, computes partial results in parallel and reduces them;
+ *     PagedAttention reads KV stored in non-contiguous fixed-size blocks) and
+ *     the related-work page (CuFlash-Attn), papers #5 (PagedAttention) and
+ *     #6 (grouped-query attention: each group of query heads shares one K/V
+ *     head).
+ *   - Library shape: the related-work page's repository comparison and
+ *     "zero dependency" positioning (a standalone dynamic library callable
+ *     through ctypes, head_dim in {32, 64, 128}, full forward and backward).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layouts (dense, row-major, element strides implied by the shapes):
+ *     Q, O, dO, dQ : [B, Hq,  Nq, d]
+ *     K, V, dK, dV : [B, Hkv, Nk, d]
+ *     LSE          : [B, Hq,  Nq]  float32, natural-log logsumexp of each
+ *                    scaled, masked score row (LSE = m + ln l).
+ *   Query head h reads K/V head h / (Hq / Hkv) (contiguous groups); Hq must
+ *   be a multiple of Hkv (Hkv == Hq: multi-head; Hkv == 1: multi-query).
+ *   dtype is one of FA_F32, FA_F16, FA_BF16 and applies to every tensor
+ *   except LSE, the workspaces and the integer decode metadata.  Products run
+ *   on the matrix cores with float32 accumulation; the probabilities P (and
+ *   dS in the backward) are rounded to dtype before their second product
+ *   (round-to-nearest-even), except for FA_F32 which keeps float32 throughout.
+ *   causal != 0 applies the bottom-right aligned mask: query row i sees key j
+ *   iff j <= i + (Nk - Nq).  Rows that see no key (only when Nq > Nk) produce
+ *   O = 0, LSE = -inf and zero gradients.
+ *   scale is applied to Q Kᵀ before the mask and the softmax (1/sqrt(d) is
+ *   customary; any finite value is accepted).
+ *   Pointers are device pointers (hipMalloc'd or torch CUDA tensors) unless
+ *   stated; all are owned by the caller.  The library allocates nothing,
+ *   keeps no pointer after a call returns and holds no mutable global state.
+ *   Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL means the default stream); results are valid after the caller
+ *   synchronises that stream.
+ *   Arguments are validated on the host before any HIP call; a failed
+ *   validation returns its error code and leaves every buffer untouched.
+ *   FA_ERR_LAUNCH reports a failure of the kernel launch itself.  No entry
+ *   point throws or aborts.
+ */
+#ifndef FLASH_ATTN_MI355X_H
+#define FLASH_ATTN_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+  FA_ERR_SHAPE = 2,     /* a size is <= 0 (or < 0 where 0 is allowed), or too large     */
+  FA_ERR_HEADDIM = 3,   /* d not in {32, 64, 128}                                       */
+  FA_ERR_DTYPE = 4,     /* dtype not one of enum fa_dtype                               */
+  FA_ERR_GQA = 5,       /* Hq is not a multiple of Hkv                                  */
+  FA_ERR_BLOCKSIZE = 6, /* decode page size other than 16 tokens                        */
+  FA_ERR_WORKSPACE = 7, /* workspace pointer NULL or smaller than the size query says   */
+  FA_ERR_LAUNCH = 8,    /* a kernel launch failed (hipGetLastError after the launch)    */
+  FA_ERR_SCALE = 9      /* scale is not finite                                          */
+};
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* flash_attn_strerror(int code);
+
+/*
+ * Forward.  Inputs Q, K, V; outputs O (dtype) and LSE (float32, one value per
+ * query row, needed by the backward).  Sizes: B, Hq, Hkv, Nq, Nk >= 1;
+ * d in {32, 64, 128}; B*Hq*Nq*d and B*Hkv*Nk*d below 2^31 elements.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_GQA,
+ * FA_ERR_SCALE, FA_ERR_LAUNCH.
+ */
+int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs (float32 row terms
+ * D_i = sum_c dO_ic * O_ic, one per query row).  Returns 0 for invalid sizes.
+ */
+size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype);
+
+/*
+ * Backward.  Inputs Q, K, V, the forward's O and LSE, and the upstream
+ * gradient dO; outputs dQ, dK, dV (dtype; fully overwritten, not
+ * accumulated into).  dK and dV of a K/V head are summed over the query heads
+ * of its group.  workspace must hold flash_attn_bwd_workspace_bytes(...)
+ * bytes; its contents on entry are ignored.  Deterministic: identical inputs
+ * give bitwise identical outputs.
+ * Errors: as flash_attn_fwd, plus FA_ERR_WORKSPACE.
+ */
+int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* dQ, void* dK, void* dV,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Number of KV splits the decode uses for num_splits = 0 (automatic): enough
+ * work-groups to cover the 256 compute units several times over, with at
+ * least 4 pages per split.  Pure host arithmetic, no HIP call.
+ */
+int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size);
+
+/*
+ * Bytes of device workspace flash_attn_decode_paged needs for the given
+ * split count (0 = automatic, resolved as above): per (sequence, query head,
+ * split) a float32 partial output of d values and its running max and sum.
+ * Returns 0 for invalid sizes.
+ */
+size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq,
+                                         int block_size, int num_splits);
+
+/*
+ * Split-KV decode of one new query token per sequence over a paged KV cache.
+ *   Q        [B, Hq, d]                            (the token's queries)
+ *   K_cache  [num_blocks, Hkv, block_size, d]      (pages; token t of sequence
+ *   V_cache  [num_blocks, Hkv, block_size, d]       b is slot t % block_size of
+ *                                                   page block_table[b][t / block_size])
+ *   block_table [B, max_blocks_per_seq] int32 device array of page ids in
+ *               [0, num_blocks); entries past a sequence's last page are
+ *               never read.  Out-of-range ids are not checked (undefined).
+ *   seq_lens    [B] int32 device array, 0 <= seq_lens[b] <=
+ *               max_blocks_per_seq * block_size (tokens of sequence b; the
+ *               tail of its last page is ignored).  A length of 0 gives O = 0
+ *               and LSE = -inf.
+ *   O   [B, Hq, d] dtype;  LSE [B, Hq] float32, or NULL if not wanted.
+ * The query is the sequence's last position, so it sees every cached token
+ * (no mask).  Each split runs an online softmax over its share of the pages;
+ * a second kernel merges the splits' (max, sum, output) partials.
+ * block_size must be 16.  num_splits >= 0 (0 = automatic); results depend on
+ * the split count only through float32 rounding order.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_GQA,
+ * FA_ERR_BLOCKSIZE, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_LAUNCH.
+ */
+int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                            const int* block_table, const int* seq_lens, void* O, float* LSE,
+                            int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                            int num_blocks, float scale, int num_splits, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_MI355X_H */
