@@ -24,7 +24,7 @@ _DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_
 
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
-    5: "FA_ERR_GQA", 6: "FA_ERR_BLOCKSIZE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_SCALE",
+    5: "FA_ERR_GQA", 6: "FA_ERR_BLOCKSIZE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_SCALE", 10: "FA_ERR_ALIGN",
 }
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t

@@ -30,6 +30,8 @@ int check_dense(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int 
   return FA_OK;
 }
 
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 }  // namespace
@@ -48,6 +50,7 @@ const char* flash_attn_strerror(int code) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes; LSE and int32 arrays 4 bytes)";
   }
   return "unknown error code";
 }
@@ -57,6 +60,8 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
   const int st = check_dense(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FA_ERR_ALIGN;
   fa::FwdArgs a;
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
@@ -66,7 +71,7 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
 
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype) {
   if (check_dense(B, Hq, Hkv, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
-  return (size_t)B * Hq * Nq * sizeof(float);
+  return 2 * (size_t)B * Hq * Nq * sizeof(float);  // D row terms, then LSE * log2(e)
 }
 
 int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
@@ -77,6 +82,9 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
   if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype))
     return FA_ERR_WORKSPACE;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+      !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
   fa::BwdArgs a;
   a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
   a.dq = dQ; a.dk = dK; a.dv = dV; a.dsum = (float*)workspace;
@@ -123,6 +131,9 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
   if (!workspace ||
       workspace_bytes < flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, splits))
     return FA_ERR_WORKSPACE;
+  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(O, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(LSE, 4) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
   fa::DecodeArgs a;
   a.q = Q; a.k_cache = K_cache; a.v_cache = V_cache; a.block_table = block_table; a.seq_lens = seq_lens;
   a.o = O; a.lse = LSE; a.part = (float*)workspace;

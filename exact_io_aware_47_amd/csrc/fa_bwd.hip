@@ -1,5 +1,477 @@
+// fa_bwd.hip -- exact attention backward for gfx950 (recomputation).
+//
+// The tutorial "FlashAttention and efficient attention kernels" (sections
+// "Backward" and "Backward recompute flow") and the concept page
+// "Flash-Attention" ("Core idea": recomputation instead of stored softmax
+// intermediates) fix the flow: reload Q, K, V blocks and the saved per-row
+// statistics, rebuild S and P on chip, combine with dO into dQ, dK, dV, and
+// drop every block once used.  The pages print no gradient formula; the
+// kernels evaluate the chain rule of the three-step definition:
+//   P  = exp(scale*S - LSE)          (no running max needed: LSE is final)
+//   dV = Pᵀ dO,   dP = dO Vᵀ,   dS = P ∘ (dP - D),   D_i = Σ_c dO_ic O_ic
+//   dQ = scale dS K,   dK = scale dSᵀ Q
+//
+// Three kernels, all deterministic (no atomics):
+//   bwd_prep : D_i and LSE_i*log2(e) per query row (a streaming pass);
+//   bwd_dkdv : KV-outer.  A work-group keeps 128 keys (32 per wave) and their
+//              K, V rows in registers and walks every query tile (of every
+//              query head of its group) that can see them.  S = Q Kᵀ is
+//              computed with queries as the A rows and keys as lanes, so P
+//              and dS come out in exactly the B-operand layout of dVᵀ += dOᵀ P
+//              and dKᵀ += Qᵀ dS; Qᵀ and dOᵀ come from transposing LDS reads.
+//   bwd_dq   : Q-outer, shaped like the forward: Sᵀ = K Qᵀ and dPᵀ = V dOᵀ
+//              with queries as lanes, then dQᵀ += Kᵀ dSᵀ.
+// P and dS are rounded to the input type before their products (float32
+// inputs keep float32).
 #include "fa_device.hpp"
 #include "fa_kernels.h"
+
 namespace fa {
-hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+// ---------------------------------------------------------------------------
+// Preprocess
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ dsum,
+                                                       float* __restrict__ lse2, int64_t rows) {
+  constexpr int kES = (int)sizeof(T);
+  constexpr int kEPC = 16 / kES;  // elements per 16-byte chunk
+  constexpr int kTPR = D / kEPC;  // threads per row (4..32)
+  typedef T tv __attribute__((ext_vector_type(kEPC)));
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / kTPR;
+  const int c = (int)(gid % kTPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const tv a = __builtin_bit_cast(tv, *(const u32x4*)(o + row * D + c * kEPC));
+    const tv b = __builtin_bit_cast(tv, *(const u32x4*)(dout + row * D + c * kEPC));
+#pragma unroll
+    for (int i = 0; i < kEPC; i++) acc = fmaf((float)a[i], (float)b[i], acc);
+  }
+#pragma unroll
+  for (int off = kTPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && c == 0) {
+    dsum[row] = acc;
+    const float L = lse[row];
+    // Rows that see no key carry LSE = -inf; +inf makes exp2(s - lse2) vanish.
+    lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
+  }
 }
+
+// ---------------------------------------------------------------------------
+// dK, dV (KV-outer)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DkvCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kBKV = 32 * kWaves;  // keys per work-group
+  static constexpr int kES = Elem<T>::kBytes;
+  static constexpr int kRowBytes = D * kES;
+  static constexpr int kBQ = 64;            // query rows per step
+  static constexpr int kKS = D / 16;
+  static constexpr int kMT = kBQ / 32;      // 32-query M tiles of S
+  static constexpr int kPS = kBQ / 16;      // 16-query k blocks of dVᵀ/dKᵀ
+  static constexpr int kDT = D / 32;
+  static constexpr int kTileBytes = kBQ * kRowBytes;
+  static constexpr int kStatBytes = 2 * kBQ * 4;  // lse2, dsum of the step's rows
+  static constexpr int kBufBytes = 2 * kTileBytes + kStatBytes;
+  static constexpr int kLds = 2 * kBufBytes;
+  static_assert(kStatBytes == 512, "stats are staged by 32 lanes x 16 B");
+};
+
+struct DkvParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse2;
+  const float* dsum;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nk;
+  int n_ktiles;
+  float c;      // scale * log2(e)
+  float scale;
+};
+
+// Eight consecutive floats of the LDS stats area starting at float index i.
+__device__ __forceinline__ void lds_read8f(const lds_char* base, int i, float* out) {
+  const u32x4 a = lds_read16(base, (uint32_t)i * 4), b = lds_read16(base, (uint32_t)i * 4 + 16);
+#pragma unroll
+  for (int j = 0; j < 4; j++) { out[j] = as_float(a[j]); out[4 + j] = as_float(b[j]); }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void bwd_dkdv_kernel(DkvParams p) {
+  using C = DkvCfg<T, D>;
+  using E = Elem<T>;
+  using F = Frags<T>;
+  using TT = Tile<C::kRowBytes>;
+  typedef typename E::Frag Frag;
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  // Block -> (key tile, batch, kv head).  Under the causal mask the first key
+  // tiles are seen by the most query rows, so they go first.
+  const int bh_count = p.B * p.Hkv;
+  const int id = blockIdx.x;
+  const int bhk = id % bh_count;
+  const int kt = id / bh_count;
+  const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
+  const int g = p.Hq / p.Hkv;
+
+  const int lane = lane_id(), w = wave_id();
+  const int h = lane >> 5, col = lane & 31;
+  const int k0 = kt * C::kBKV;
+  const int kw = k0 + 32 * w;   // first key of this wave
+  const int key = kw + col;     // this lane's key
+  const int diag = p.Nk - p.Nq; // key j is visible to row i iff j <= i + diag (causal)
+
+  const size_t kv_slab = (size_t)bhk * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+
+  // Query tiles that can see this work-group's keys, for each head of the group.
+  const int n_qt = (p.Nq + C::kBQ - 1) / C::kBQ;
+  const int qt0 = CAUSAL ? max(0, k0 - diag) / C::kBQ : 0;
+  const int per_head = n_qt - qt0;
+  const int steps = g * per_head;
+
+  auto load_step = [&](int s, int buf) {
+    const int hq = hkv * g + s / per_head;
+    const int qt = qt0 + s % per_head;
+    const size_t bhq = (size_t)b * p.Hq + hq;
+    const size_t q_slab = bhq * p.Nq * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+    lds_char* qb = smem + buf * C::kBufBytes;
+    const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, qb, w, lane);
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, qb + C::kTileBytes, w, lane);
+    // Per-row stats of the step: lanes 0-15 stage lse2, lanes 16-31 dsum.
+    if (w == 0) {
+      const uint32_t off = (uint32_t)qt * C::kBQ * 4 + (lane & 15) * 16;
+      if (lane < 16) buf_load16_to_lds(make_rsrc(p.lse2 + bhq * p.Nq, (uint32_t)p.Nq * 4), off, qb + 2 * C::kTileBytes);
+      else if (lane < 32) buf_load16_to_lds(make_rsrc(p.dsum + bhq * p.Nq, (uint32_t)p.Nq * 4), off, qb + 2 * C::kTileBytes);
+    }
+  };
+
+  if (steps > 0) load_step(0, 0);
+
+  // Kᵀ and Vᵀ as B operands (k = d, column = this lane's key).
+  Frag kf[C::kKS], vf[C::kKS];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ks++) {
+    kf[ks] = F::template global_row<D>(rk, key, ks, h);
+    vf[ks] = F::template global_row<D>(rv, key, ks, h);
+  }
+  f32x16 dk[C::kDT], dv[C::kDT];
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
+
+  wait_vmem();
+  __syncthreads();
+
+  for (int s = 0; s < steps; s++) {
+    const int buf = s & 1;
+    if (s + 1 < steps) load_step(s + 1, buf ^ 1);
+    const lds_char* qb = smem + buf * C::kBufBytes;
+    const lds_char* dob = qb + C::kTileBytes;
+    const lds_char* stb = qb + 2 * C::kTileBytes;
+    const int i0 = (qt0 + s % per_head) * C::kBQ;  // first query row of the step
+
+    if (!CAUSAL || i0 + C::kBQ - 1 + diag >= kw) {
+      // ---- S = Q Kᵀ and dP = dO Vᵀ; A rows are sigma-permuted queries.
+      f32x16 sv[C::kMT], dp[C::kMT];
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+#pragma unroll
+      for (int ks = 0; ks < C::kKS; ks++) {
+#pragma unroll
+        for (int mt = 0; mt < C::kMT; mt++) {
+          const int row = 32 * mt + sigma(col);
+          sv[mt] = E::mma(F::template lds_row<TT>(qb, row, ks, h), kf[ks], sv[mt]);
+          dp[mt] = E::mma(F::template lds_row<TT>(dob, row, ks, h), vf[ks], dp[mt]);
+        }
+      }
+      // ---- P and dS.  Register r of M tile mt holds query
+      //      i0 + 32*mt + 16*(r/8) + 8h + (r%8) for this lane's key.
+      const bool need_mask = CAUSAL && kw + 31 > i0 + diag;
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          float l2[8], dd[8];
+          lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
+          lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
+#pragma unroll
+          for (int t = 0; t < 8; t++) {
+            const int r = 8 * u + t;
+            float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2[t]));
+            if (need_mask && key > i0 + 32 * mt + 16 * u + 8 * h + t + diag) pr = 0.f;
+            sv[mt][r] = pr;
+            dp[mt][r] = pr * (dp[mt][r] - dd[t]);
+          }
+        }
+      // ---- dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (column = key, k = query).
+#pragma unroll
+      for (int ps = 0; ps < C::kPS; ps++) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int t = 0; t < 8; t++) { pv[t] = sv[ps >> 1][8 * (ps & 1) + t]; dsv[t] = dp[ps >> 1][8 * (ps & 1) + t]; }
+        const Frag pf = E::pack(pv), dsf = E::pack(dsv);
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; dt++) {
+          dv[dt] = E::mma(F::template lds_col<TT>(dob, 16 * ps, 32 * dt, lane), pf, dv[dt]);
+          dk[dt] = E::mma(F::template lds_col<TT>(qb, 16 * ps, 32 * dt, lane), dsf, dk[dt]);
+        }
+      }
+    }
+
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dKᵀ acc, dV; lane's column is its key.
+  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const uint32_t off = (uint32_t)key * C::kRowBytes + (32 * dt + 8 * a4 + 4 * h) * C::kES;
+      F::store4(wk, off, dk[dt][4 * a4] * p.scale, dk[dt][4 * a4 + 1] * p.scale, dk[dt][4 * a4 + 2] * p.scale,
+                dk[dt][4 * a4 + 3] * p.scale);
+      F::store4(wv, off, dv[dt][4 * a4], dv[dt][4 * a4 + 1], dv[dt][4 * a4 + 2], dv[dt][4 * a4 + 3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (Q-outer)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kBR = 32 * kWaves;
+  static constexpr int kES = Elem<T>::kBytes;
+  static constexpr int kRowBytes = D * kES;
+  static constexpr int kBC = (kES == 4 && D == 128) ? 32 : 64;
+  static constexpr int kKS = D / 16;
+  static constexpr int kMT = kBC / 32;
+  static constexpr int kPS = kBC / 16;
+  static constexpr int kDT = D / 32;
+  static constexpr int kTileBytes = kBC * kRowBytes;
+  static constexpr int kLds = 2 * 2 * kTileBytes;
+};
+
+struct DqParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse2;
+  const float* dsum;
+  void* dq;
+  int B, Hq, Hkv, Nq, Nk;
+  int n_qtiles;
+  float c;
+  float scale;
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(DqParams p) {
+  using C = DqCfg<T, D>;
+  using E = Elem<T>;
+  using F = Frags<T>;
+  using TT = Tile<C::kRowBytes>;
+  typedef typename E::Frag Frag;
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int bh_count = p.B * p.Hq;
+  const int id = blockIdx.x;
+  const int bh = id % bh_count;
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - id / bh_count) : id / bh_count;
+  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+
+  const int lane = lane_id(), w = wave_id();
+  const int h = lane >> 5, col = lane & 31;
+  const int q0 = qt * C::kBR;
+  const int qw = q0 + 32 * w;
+  const int qrow = qw + col;
+  const int diag = p.Nk - p.Nq;
+
+  const size_t q_slab = (size_t)bh * p.Nq * D;
+  const size_t kv_slab = ((size_t)b * p.Hkv + hkv) * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(p.lse2 + (size_t)bh * p.Nq, (uint32_t)p.Nq * 4);
+  const __amdgpu_buffer_rsrc_t rsd = make_rsrc(p.dsum + (size_t)bh * p.Nq, (uint32_t)p.Nq * 4);
+
+  int n_tiles = (p.Nk + C::kBC - 1) / C::kBC;
+  if (CAUSAL) {
+    const int last_key = min(q0 + C::kBR, p.Nq) - 1 + diag;
+    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
+  }
+
+  auto load_tile = [&](int j, int buf) {
+    lds_char* kb = smem + buf * 2 * C::kTileBytes;
+    const uint32_t g0 = (uint32_t)j * C::kBC * C::kRowBytes;
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, g0, kb, w, lane);
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, g0, kb + C::kTileBytes, w, lane);
+  };
+
+  if (n_tiles > 0) load_tile(0, 0);
+
+  Frag qf[C::kKS], dof[C::kKS];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ks++) {
+    qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
+    dof[ks] = F::template global_row<D>(rdo, qrow, ks, h);
+  }
+  const float l2 = as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)qrow * 4, 0, 0));
+  const float dd = as_float(__builtin_amdgcn_raw_buffer_load_b32(rsd, (uint32_t)qrow * 4, 0, 0));
+
+  f32x16 dq[C::kDT];
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++) dq[dt] = f32x16{};
+
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; j++) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) load_tile(j + 1, buf ^ 1);
+    const lds_char* kb = smem + buf * 2 * C::kTileBytes;
+    const lds_char* vb = kb + C::kTileBytes;
+    const int k0 = j * C::kBC;
+
+    if (!CAUSAL || k0 <= qw + 31 + diag) {
+      // ---- Sᵀ = K Qᵀ and dPᵀ = V dOᵀ; A rows are sigma-permuted keys.
+      f32x16 sv[C::kMT], dp[C::kMT];
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+#pragma unroll
+      for (int ks = 0; ks < C::kKS; ks++) {
+#pragma unroll
+        for (int mt = 0; mt < C::kMT; mt++) {
+          const int row = 32 * mt + sigma(col);
+          sv[mt] = E::mma(F::template lds_row<TT>(kb, row, ks, h), qf[ks], sv[mt]);
+          dp[mt] = E::mma(F::template lds_row<TT>(vb, row, ks, h), dof[ks], dp[mt]);
+        }
+      }
+      // ---- dSᵀ = Pᵀ ∘ (dPᵀ - D).  Register r of tile mt holds key
+      //      k0 + 32*mt + 16*(r/8) + 8h + (r%8).  Keys past Nk are masked too
+      //      (their zero-filled rows must not meet an infinite P).
+      const bool need_mask = (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
+      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
+          if (need_mask && k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) > horizon) pr = 0.f;
+          dp[mt][r] = pr * (dp[mt][r] - dd);
+        }
+      // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
+#pragma unroll
+      for (int ps = 0; ps < C::kPS; ps++) {
+        float dsv[8];
+#pragma unroll
+        for (int t = 0; t < 8; t++) dsv[t] = dp[ps >> 1][8 * (ps & 1) + t];
+        const Frag dsf = E::pack(dsv);
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; dt++)
+          dq[dt] = E::mma(F::template lds_col<TT>(kb, 16 * ps, 32 * dt, lane), dsf, dq[dt]);
+      }
+    }
+
+    wait_vmem();
+    __syncthreads();
+  }
+
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc((char*)p.dq + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const int d0 = 32 * dt + 8 * a4 + 4 * h;
+      F::store4(wq, (uint32_t)qrow * C::kRowBytes + d0 * C::kES, dq[dt][4 * a4] * p.scale,
+                dq[dt][4 * a4 + 1] * p.scale, dq[dt][4 * a4 + 2] * p.scale, dq[dt][4 * a4 + 3] * p.scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  float* dsum = a.dsum;
+  float* lse2 = a.dsum + rows;
+  {
+    constexpr int kTPR = D / (16 / (int)sizeof(T));
+    const int64_t threads = rows * kTPR;
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(grid), dim3(256), 0, stream, (const T*)a.o, (const T*)a.dout,
+                       a.lse, dsum, lse2, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const float c = a.scale * kLog2e;
+  {
+    using C = DkvCfg<T, D>;
+    DkvParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = lse2; p.dsum = dsum; p.dk = a.dk; p.dv = a.dv;
+    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+    p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
+    p.c = c; p.scale = a.scale;
+    const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    using C = DqCfg<T, D>;
+    DqParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = lse2; p.dsum = dsum; p.dq = a.dq;
+    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+    p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
+    p.c = c; p.scale = a.scale;
+    const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 32: return a.causal ? launch_typed<T, 32, true>(a, s) : launch_typed<T, 32, false>(a, s);
+    case 64: return a.causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
+    case 128: return a.causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  switch (a.dtype) {
+    case 0: return launch_dtype<float>(a, stream);
+    case 1: return launch_dtype<_Float16>(a, stream);
+    case 2: return launch_dtype<__bf16>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -140,33 +140,52 @@ __device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // --------------------------------------------------------------------------
-// LDS tiles: rows of ROW_BYTES, stored as 16-byte chunks whose position in a
-// row is XOR-permuted by a per-row key so that the access patterns of the
-// kernels hit distinct banks.
-//   TR = false: 16 consecutive rows at one chunk column hit 16 distinct
-//               16-byte bank groups (row-fragment reads).
-//   TR = true : 4 consecutive rows at an aligned group of 4 chunk columns hit
-//               distinct bank groups (transposing column-fragment reads).
+// LDS tiles: rows of ROW_BYTES stored as 16-byte chunks whose position in a
+// row is XOR-permuted by a per-row key.  The key is chosen so that both read
+// patterns of the kernels hit distinct banks (64 banks x 4 B = 256 B):
+//   row fragments   : 16 consecutive rows at one chunk column land in 16
+//                     distinct 16-byte bank groups;
+//   column fragments: 4 consecutive rows at an aligned group of 4 chunk
+//                     columns (a transposing read) land in 4 distinct
+//                     64-byte bank segments.
+// With 16+ chunks per row the key 4*(row%4) + (row/4)%4 is a bijection on 16
+// rows and spreads any 4 consecutive rows over the 4 segments; with 8 chunks
+// (two rows per 256 B) bit 2 of the key is bit 1 of the row; with 4 chunks
+// (four rows per 256 B) the row itself picks the segment.
 // --------------------------------------------------------------------------
-template <int ROW_BYTES, bool TR>
+template <int ROW_BYTES>
 struct Tile {
-  static constexpr int kChunks = ROW_BYTES / 16;                       // chunks per row
-  static constexpr int kRowsPerSweep = kChunks >= 16 ? 1 : 16 / kChunks;  // rows per 256 B
-  static constexpr int kKeyMask = (kChunks >= 16 ? 16 : kChunks) - 1;
+  static constexpr int kChunks = ROW_BYTES / 16;  // chunks per row
+  static_assert(kChunks == 4 || kChunks == 8 || kChunks % 16 == 0, "unsupported row size");
   __device__ static __forceinline__ int key(int row) {
-    if constexpr (!TR) {
-      return (row / kRowsPerSweep) & kKeyMask;
-    } else {
-      if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-      else if constexpr (kChunks == 8) return ((row >> 1) & 1) << 2;
-      else return 0;
-    }
+    if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (kChunks == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else return (row >> 2) & 3;
   }
   // byte offset of logical chunk c of row `row`
   __device__ static __forceinline__ uint32_t off(int row, int c) {
     return (uint32_t)(row * ROW_BYTES + ((c ^ key(row)) << 4));
   }
 };
+
+// Stage ROWS rows of ROW_BYTES, starting at byte g0 of resource r, into a
+// swizzled LDS tile.  The tile splits into 1 KiB slices of 64 lanes x 16 B;
+// each of the WAVES waves moves an equal share.  Physical slot s holds logical
+// chunk (s % chunks) ^ key(row) of row s / chunks; rows past the resource's
+// range read as zero.
+template <int ROW_BYTES, int ROWS, int WAVES>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, uint32_t g0, lds_char* tile, int w, int lane) {
+  using TT = Tile<ROW_BYTES>;
+  constexpr int kSlices = ROWS * ROW_BYTES / 1024;
+  static_assert(kSlices * 1024 == ROWS * ROW_BYTES && kSlices % WAVES == 0, "tile must split into whole wave slices");
+#pragma unroll
+  for (int i = 0; i < kSlices / WAVES; i++) {
+    const int s0 = (w * (kSlices / WAVES) + i) * 64;
+    const int s = s0 + lane;
+    const int row = s / TT::kChunks, pc = s % TT::kChunks;
+    buf_load16_to_lds(r, g0 + row * ROW_BYTES + ((pc ^ TT::key(row)) << 4), tile + s0 * 16);
+  }
+}
 
 __device__ __forceinline__ u32x4 lds_read16(const lds_char* base, uint32_t off) {
   return *(const __attribute__((address_space(3))) u32x4*)(base + off);

@@ -36,9 +36,7 @@ struct FwdCfg {
   static constexpr int kPS = kBC / 16;                       // 16-key k blocks of V^T P^T
   static constexpr int kDT = D / 32;                         // 32-row M tiles of O^T
   static constexpr int kTileBytes = kBC * kRowBytes;
-  static constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;
   static constexpr int kLds = 2 * 2 * kTileBytes;            // {K, V} x double buffer
-  static_assert(kDmaPerWave * 1024 * kWaves == kTileBytes, "tile must split into whole 1 KiB wave loads");
 };
 
 struct FwdParams {
@@ -58,8 +56,7 @@ void fwd_kernel(FwdParams p) {
   using C = FwdCfg<T, D>;
   using E = Elem<T>;
   using F = Frags<T>;
-  using KT = Tile<C::kRowBytes, false>;  // K: row-fragment reads
-  using VT = Tile<C::kRowBytes, true>;   // V: transposing column-fragment reads
+  using TT = Tile<C::kRowBytes>;
   typedef typename E::Frag Frag;
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
@@ -93,21 +90,12 @@ void fwd_kernel(FwdParams p) {
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
 
-  // Stage K/V tile j into LDS buffer `buf`: each wave moves kDmaPerWave KiB of
-  // each; physical 16-byte slot s of the tile holds logical chunk
-  // (s % chunks) ^ key(row) of row s / chunks.  Keys past Nk read as zero.
+  // Stage K/V tile j into LDS buffer `buf` (keys past Nk read as zero).
   auto load_tile = [&](int j, int buf) {
     lds_char* kb = smem + buf * 2 * C::kTileBytes;
-    lds_char* vb = kb + C::kTileBytes;
     const uint32_t g0 = (uint32_t)j * C::kBC * C::kRowBytes;
-#pragma unroll
-    for (int i = 0; i < C::kDmaPerWave; i++) {
-      const int s0 = (w * C::kDmaPerWave + i) * 64;
-      const int s = s0 + lane;
-      const int row = s / KT::kChunks, pc = s % KT::kChunks;
-      buf_load16_to_lds(rk, g0 + row * C::kRowBytes + ((pc ^ KT::key(row)) << 4), kb + s0 * 16);
-      buf_load16_to_lds(rv, g0 + row * C::kRowBytes + ((pc ^ VT::key(row)) << 4), vb + s0 * 16);
-    }
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, g0, kb, w, lane);
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, g0, kb + C::kTileBytes, w, lane);
   };
 
   if (n_tiles > 0) load_tile(0, 0);
@@ -144,7 +132,7 @@ void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < C::kKS; ks++) {
 #pragma unroll
         for (int mt = 0; mt < C::kMT; mt++) {
-          const Frag a = F::template lds_row<KT>(kb, 32 * mt + sigma(col), ks, h);
+          const Frag a = F::template lds_row<TT>(kb, 32 * mt + sigma(col), ks, h);
           s[mt] = E::mma(a, qf[ks], s[mt]);
         }
       }
@@ -208,7 +196,7 @@ void fwd_kernel(FwdParams p) {
         const Frag pf = E::pack(pv);
 #pragma unroll
         for (int dt = 0; dt < C::kDT; dt++) {
-          const Frag a = F::template lds_col<VT>(vb, 16 * ps, 32 * dt, lane);
+          const Frag a = F::template lds_col<TT>(vb, 16 * ps, 32 * dt, lane);
           o[dt] = E::mma(a, pf, o[dt]);
         }
       }

@@ -77,7 +77,9 @@ enum fa_status {
   FA_ERR_BLOCKSIZE = 6, /* decode page size other than 16 tokens                        */
   FA_ERR_WORKSPACE = 7, /* workspace pointer NULL or smaller than the size query says   */
   FA_ERR_LAUNCH = 8,    /* a kernel launch failed (hipGetLastError after the launch)    */
-  FA_ERR_SCALE = 9      /* scale is not finite                                          */
+  FA_ERR_SCALE = 9,     /* scale is not finite                                          */
+  FA_ERR_ALIGN = 10     /* a pointer is misaligned: dtype tensors and workspaces need   */
+                        /* 16-byte alignment, LSE and int32 arrays 4-byte alignment     */
 };
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -87,16 +89,18 @@ const char* flash_attn_strerror(int code);
  * Forward.  Inputs Q, K, V; outputs O (dtype) and LSE (float32, one value per
  * query row, needed by the backward).  Sizes: B, Hq, Hkv, Nq, Nk >= 1;
  * d in {32, 64, 128}; B*Hq*Nq*d and B*Hkv*Nk*d below 2^31 elements.
- * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_GQA,
- * FA_ERR_SCALE, FA_ERR_LAUNCH.
+ * Errors (checked in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_SHAPE (too large), FA_ERR_SCALE,
+ * FA_ERR_ALIGN, then FA_ERR_LAUNCH.
  */
 int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                    int dtype, void* stream);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs (float32 row terms
- * D_i = sum_c dO_ic * O_ic, one per query row).  Returns 0 for invalid sizes.
+ * Bytes of device workspace flash_attn_bwd needs: two float32 values per query
+ * row (the row term D_i = sum_c dO_ic * O_ic and LSE_i * log2(e)).  Returns 0
+ * for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype);
 
@@ -107,7 +111,7 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, in
  * of its group.  workspace must hold flash_attn_bwd_workspace_bytes(...)
  * bytes; its contents on entry are ignored.  Deterministic: identical inputs
  * give bitwise identical outputs.
- * Errors: as flash_attn_fwd, plus FA_ERR_WORKSPACE.
+ * Errors: as flash_attn_fwd, with FA_ERR_WORKSPACE checked before FA_ERR_ALIGN.
  */
 int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV,
@@ -149,8 +153,9 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  * a second kernel merges the splits' (max, sum, output) partials.
  * block_size must be 16.  num_splits >= 0 (0 = automatic); results depend on
  * the split count only through float32 rounding order.
- * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_GQA,
- * FA_ERR_BLOCKSIZE, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_LAUNCH.
+ * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
+ * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_LAUNCH.
  */
 int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
                             const int* block_table, const int* seq_lens, void* O, float* LSE,
