@@ -110,7 +110,7 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
       block_size != 16 || num_splits < 0)
     return 0;
   const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
-  return (size_t)B * Hq * splits * (d + 2) * sizeof(float);
+  return (size_t)B * Hq * splits * (d + 4) * sizeof(float);  // [O (d), m, l, 2 pad] per split
 }
 
 int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
@@ -118,14 +118,13 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
                             int max_blocks_per_seq, int num_blocks, float scale, int num_splits, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !O) return FA_ERR_NULL;
-  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_splits < 0)
     return FA_ERR_SHAPE;
   if (!headdim_ok(d)) return FA_ERR_HEADDIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   if (block_size != 16) return FA_ERR_BLOCKSIZE;
-  if ((int64_t)num_blocks * Hkv * block_size * d >= kMaxElems || (int64_t)B * max_blocks_per_seq >= kMaxElems)
-    return FA_ERR_SHAPE;
+  if ((int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)B * Hq * d >= kMaxElems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
   if (!workspace ||

@@ -1,5 +1,309 @@
+// fa_decode.hip -- split-KV decode over a paged KV cache for gfx950.
+//
+// FlashDecoding and PagedAttention as the tutorial "FlashAttention and
+// efficient attention kernels" describes them ("Variant family"): the KV
+// sequence of each new token is cut into splits whose partial softmax results
+// are computed in parallel and reduced afterwards, and the keys/values are
+// read from fixed-size pages reached through a block table.  Grouped-query
+// heads follow the related-work page's paper #6: the query heads of one group
+// share a K/V head, so they are processed together against each page.
+//
+// decode_split: every wave is one split of one (sequence, K/V head, group of
+//   up to 16 query heads).  It walks its pages two at a time through a
+//   private double-buffered LDS ring (bounds-checked buffer-to-LDS loads, one
+//   descriptor per page, so token slots past the sequence end read as zero):
+//     Sᵀ = K_page Qᵀ          (16 tokens x 16 query heads, 16x16x32 MFMA)
+//     online softmax per query head (running max m, running sum l, log2 domain)
+//     Oᵀ = Oᵀ exp2(m_old - m_new) + Vᵀ Pᵀ   (32 tokens per product; Vᵀ comes
+//                                           from transposing LDS reads)
+//   and writes its partial (Oᵀ unnormalised, m, l) to the workspace as a
+//   16-byte aligned record of D + 4 floats.
+// decode_reduce: merges the splits of each query head (the tutorial's
+//   correction formula applied to every split against the common max):
+//     M = max m_s,  L = Σ l_s 2^(m_s - M),  O = Σ O_s 2^(m_s - M) / L,
+//     LSE = (M + log2 L) ln 2.
 #include "fa_device.hpp"
 #include "fa_kernels.h"
+
 namespace fa {
-hipError_t launch_decode(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mma16;
+template <> struct Mma16<__bf16> {
+  __device__ static __forceinline__ f32x4v mma(const bf16x8& a, const bf16x8& b, const f32x4v& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<_Float16> {
+  __device__ static __forceinline__ f32x4v mma(const f16x8& a, const f16x8& b, const f32x4v& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T, int D>
+struct DecCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kPage = 16;                 // tokens per page
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kPageBytes = kPage * kRowBytes;
+  static constexpr int kSlices = kPageBytes / 1024;  // 1 KiB wave loads per page
+  static constexpr int kStageBytes = 4 * kPageBytes;  // K and V of two pages
+  static constexpr int kWaveBytes = 2 * kStageBytes;  // double buffer
+  static constexpr int kLds = kWaves * kWaveBytes;
+  static constexpr int kKS = D / 32;               // 32-wide k blocks along d
+  static constexpr int kDT = D / 16;               // 16-row M tiles of Oᵀ
+  static_assert(kSlices >= 1 && kSlices * 1024 == kPageBytes, "page must split into 1 KiB loads");
+};
+
+struct SplitParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  int B, Hq, Hkv, max_blocks, num_blocks, splits, n_qc;
+  float c;
+};
+
+// The block table and sequence lengths are separate restrict-qualified
+// arguments so that the compiler can prove them read-only and fetch them with
+// scalar loads: a vector load would make the wave wait for every outstanding
+// page load (they share one counter) and stall the pipeline each page.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const int* __restrict__ block_table,
+                                                           const int* __restrict__ seq_lens,
+                                                           float* __restrict__ part) {
+  using C = DecCfg<T, D>;
+  using TT = Tile<C::kRowBytes>;
+  typedef typename Elem<T>::Frag Frag;
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
+  const int lane = lane_id(), w = wave_id();
+  const int unit = blockIdx.x * C::kWaves + w;  // (split, query column tile) of this wave
+  if (unit >= p.splits * p.n_qc) return;         // no barriers in this kernel
+  const int split = unit / p.n_qc, qc = unit - split * p.n_qc;
+  const int bhk = blockIdx.y;
+  const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
+  const int g = p.Hq / p.Hkv;
+  lds_char* ring = (lds_char*)smem_raw + w * C::kWaveBytes;
+
+  const int i16 = lane & 15, G = lane >> 4;
+  const int qi = qc * 16 + i16;                  // query head within the group (column)
+  const bool q_ok = qi < g;
+  const int hq = hkv * g + qi;
+
+  const int seq_len = seq_lens[b];
+  const int n_pages = (seq_len + C::kPage - 1) / C::kPage;
+  const int pg0 = (int)((int64_t)n_pages * split / p.splits);
+  const int pg1 = (int)((int64_t)n_pages * (split + 1) / p.splits);
+  const int tok_end = min(seq_len, pg1 * C::kPage);
+  const int* table = block_table + (size_t)b * p.max_blocks;
+
+  // Stage pages pg, pg+1 (K then V) into ring buffer `st`.  Pages at or past
+  // pg1 get an empty range, slots past the sequence end are clipped.
+  auto load_pair = [&](int pg, int st) {
+    lds_char* sb = ring + st * C::kStageBytes;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int page_idx = pg + u;
+      uint32_t bytes = 0;
+      size_t base = 0;
+      if (page_idx < pg1) {
+        const int page = table[page_idx];
+        if (page >= 0 && page < p.num_blocks) {  // a bad table entry reads as a page of zeros
+          base = ((size_t)page * p.Hkv + hkv) * C::kPageBytes;
+          bytes = (uint32_t)min(C::kPage, seq_len - page_idx * C::kPage) * C::kRowBytes;
+        }
+      }
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.kc + base, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.vc + base, bytes);
+#pragma unroll
+      for (int i = 0; i < C::kSlices; i++) {
+        const int s = i * 64 + lane;
+        const int row = s / TT::kChunks, pc = s % TT::kChunks;
+        const uint32_t off = row * C::kRowBytes + ((pc ^ TT::key(row)) << 4);
+        buf_load16_to_lds(rk, off, sb + u * C::kPageBytes + i * 1024);
+        buf_load16_to_lds(rv, off, sb + (2 + u) * C::kPageBytes + i * 1024);
+      }
+    }
+  };
+
+  const int n_pairs = (pg1 - pg0 + 1) / 2;
+  if (n_pairs > 0) load_pair(pg0, 0);
+
+  // Qᵀ as the B operand: column = query head, k = d (8 per lane per 32-wide block).
+  Frag qf[C::kKS];
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc((const char*)p.q + ((size_t)b * p.Hq + hkv * g) * C::kRowBytes, (uint32_t)g * C::kRowBytes);
+    const uint32_t qoff = q_ok ? (uint32_t)qi * C::kRowBytes : 0xFFFFFFF0u;
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ks++)
+      qf[ks] = __builtin_bit_cast(Frag, buf_load16(rq, qoff + (32 * ks + 8 * G) * 2));
+  }
+
+  f32x4v o[C::kDT];
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++) o[dt] = f32x4v{};
+  float m = -INFINITY, l = 0.f;
+
+  for (int i = 0; i < n_pairs; i++) {
+    const int st = i & 1;
+    if (i + 1 < n_pairs) {
+      load_pair(pg0 + 2 * (i + 1), st ^ 1);
+      // Wait for the older stage only: the newer pair's loads may stay in flight.
+      // (A pair is 4 * kSlices loads; loads retire in issue order.)
+      if constexpr (C::kSlices == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (C::kSlices == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      wait_vmem();
+    }
+    const lds_char* kb = ring + st * C::kStageBytes;
+    const lds_char* vb = kb + 2 * C::kPageBytes;
+    const int t0 = (pg0 + 2 * i) * C::kPage;  // first token of the pair
+
+    // ---- Sᵀ for both pages: register r of page u holds token t0 + 16u + 4G + r.
+    f32x4v s[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      s[u] = f32x4v{};
+#pragma unroll
+      for (int ks = 0; ks < C::kKS; ks++) {
+        const Frag a = __builtin_bit_cast(Frag, lds_read16(kb + u * C::kPageBytes, TT::off(i16, 4 * ks + G)));
+        s[u] = Mma16<T>::mma(a, qf[ks], s[u]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float t = (t0 + 16 * u + 4 * G + r) < tok_end ? s[u][r] * p.c : -INFINITY;
+        s[u][r] = t;
+        mx = fmaxf(mx, t);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float pv[8], rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float e = fast_exp2(s[u][r] - m_use);
+        pv[4 * u + r] = e;
+        rs += e;
+      }
+    l = l * alpha + rs;
+    m = m_new;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; dt++) o[dt] *= alpha;
+    }
+    const Frag pf = Elem<T>::pack(pv);  // slot t: token 4G + t of page 0 (t < 4), of page 1 (t >= 4)
+
+    // ---- Oᵀ += Vᵀ Pᵀ.  Vᵀ slot t of lane (d = 16dt + i16, G) is V[token of slot t][d].
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; dt++) {
+      const int row = 4 * G + (i16 >> 2);
+      const int col = 16 * dt + 4 * (lane & 3);
+      const uint32_t off = TT::off(row, col >> 3) + ((col & 7) << 1);
+      const i16x4 v0 = lds_read_tr16(vb, off);
+      const i16x4 v1 = lds_read_tr16(vb + C::kPageBytes, off);
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 a8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      o[dt] = Mma16<T>::mma(__builtin_bit_cast(Frag, a8), pf, o[dt]);
+    }
+  }
+
+  // ---- partial result: Oᵀ (unnormalised), m, l (summed over the 4 lane groups).
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (q_ok) {
+    const size_t rec = (((size_t)b * p.Hq + hq) * p.splits + split) * (D + 4);
+    float* dst = part + rec;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; dt++) {
+      f32x4v v = o[dt];
+      *(f32x4v*)(dst + 16 * dt + 4 * G) = v;  // d = 16dt + 4G + 0..3
+    }
+    if (G == 0) { dst[D] = m; dst[D + 1] = l; }
+  }
 }
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, T* __restrict__ out,
+                                                           float* __restrict__ lse, int splits) {
+  const int bh = blockIdx.x;
+  const float* rec = part + (size_t)bh * splits * (D + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; s++) M = fmaxf(M, rec[(size_t)s * (D + 4) + D]);
+  float L = 0.f;
+  constexpr int kPer = D / 64 > 0 ? D / 64 : 1;
+  float acc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) acc[j] = 0.f;
+  for (int s = 0; s < splits; s++) {
+    const float* r = rec + (size_t)s * (D + 4);
+    const float ms = r[D];
+    const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+    L = fmaf(r[D + 1], wgt, L);
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int d = threadIdx.x + 64 * j;
+      if (d < D) acc[j] = fmaf(r[d], wgt, acc[j]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int d = threadIdx.x + 64 * j;
+    if (d < D) out[(size_t)bh * D + d] = (T)(acc[j] * inv);
+  }
+  if (lse != nullptr && threadIdx.x == 0) lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  using C = DecCfg<T, D>;
+  SplitParams p;
+  p.q = a.q; p.kc = a.k_cache; p.vc = a.v_cache; p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.max_blocks = a.max_blocks; p.num_blocks = a.num_blocks;
+  p.splits = a.splits;
+  const int g = a.Hq / a.Hkv;
+  p.n_qc = (g + 15) / 16;
+  p.c = a.scale * kLog2e;
+  const int units = a.splits * p.n_qc;
+  dim3 grid((units + C::kWaves - 1) / C::kWaves, a.B * a.Hkv);
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(64 * C::kWaves), 0, stream, p, a.block_table,
+                     a.seq_lens, a.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream, a.part, (T*)a.o, a.lse,
+                     a.splits);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(const DecodeArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 32: return launch_typed<T, 32>(a, s);
+    case 64: return launch_typed<T, 64>(a, s);
+    case 128: return launch_typed<T, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dtype) {
+    case 1: return launch_dtype<_Float16>(a, stream);
+    case 2: return launch_dtype<__bf16>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

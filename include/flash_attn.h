@@ -128,8 +128,8 @@ int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int blo
 /*
  * Bytes of device workspace flash_attn_decode_paged needs for the given
  * split count (0 = automatic, resolved as above): per (sequence, query head,
- * split) a float32 partial output of d values and its running max and sum.
- * Returns 0 for invalid sizes.
+ * split) a record of d + 4 float32 values (the partial output, its running
+ * max and sum, two pad words).  Returns 0 for invalid sizes.
  */
 size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq,
                                          int block_size, int num_splits);
@@ -142,7 +142,8 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  *                                                   page block_table[b][t / block_size])
  *   block_table [B, max_blocks_per_seq] int32 device array of page ids in
  *               [0, num_blocks); entries past a sequence's last page are
- *               never read.  Out-of-range ids are not checked (undefined).
+ *               never read.  An id outside [0, num_blocks) is read as a page
+ *               of zeros (it cannot fault, but the result is meaningless).
  *   seq_lens    [B] int32 device array, 0 <= seq_lens[b] <=
  *               max_blocks_per_seq * block_size (tokens of sequence b; the
  *               tail of its last page is ignored).  A length of 0 gives O = 0
@@ -151,8 +152,9 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  * The query is the sequence's last position, so it sees every cached token
  * (no mask).  Each split runs an online softmax over its share of the pages;
  * a second kernel merges the splits' (max, sum, output) partials.
- * block_size must be 16.  num_splits >= 0 (0 = automatic); results depend on
- * the split count only through float32 rounding order.
+ * block_size must be 16.  dtype must be FA_F16 or FA_BF16 (the float32 KV
+ * cache is not supported: FA_ERR_DTYPE).  num_splits >= 0 (0 = automatic);
+ * results depend on the split count only through float32 rounding order.
  * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
  * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
  * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_LAUNCH.

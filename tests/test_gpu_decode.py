@@ -1,0 +1,120 @@
+"""GPU parity of the split-KV paged decode against the float64 oracle."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity import assert_close, dev, f64
+from oracle import attention_f64 as orc
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa():
+    import exact_io_aware_47_amd as fa
+    return fa
+
+
+def run_decode(q, kc, vc, table, lens, scale, num_splits=0):
+    fa = _fa()
+    o, lse = fa.decode_paged(dev(q), dev(kc), dev(vc), dev(table), dev(lens), scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def oracle_decode(q, kc, vc, table, lens, scale):
+    # float32 holds every 16-bit cache value exactly; the oracle upcasts per page.
+    return orc.decode_paged(f64(q), kc.float().numpy(), vc.float().numpy(), table.numpy(), lens.numpy(), scale)
+
+
+def check(q, kc, vc, table, lens, dtype, num_splits=0):
+    sc = 1.0 / math.sqrt(q.shape[-1])
+    o, lse = run_decode(q, kc, vc, table, lens, sc, num_splits)
+    ro, rl = oracle_decode(q, kc, vc, table, lens, sc)
+    assert_close("O", f64(o), ro, dtype, "o")
+    assert_close("LSE", f64(lse), rl, dtype, "lse")
+    return o, lse
+
+
+# B, Hq, Hkv, seq_lens, d, dtype, num_splits
+CASES = [
+    (1, 1, 1, [1], 128, "bf16", 0),
+    (2, 8, 2, [17, 300], 64, "f16", 0),
+    (3, 4, 4, [16, 15, 1000], 32, "bf16", 3),
+    (4, 32, 8, [0, 5, 64, 2049], 128, "bf16", 0),
+    (2, 32, 1, [500, 33], 128, "f16", 5),       # multi-query: 32 heads share one K/V head
+    (1, 16, 1, [777], 64, "bf16", 1),
+    (2, 24, 2, [250, 1], 128, "bf16", 64),      # more splits than pages
+    (1, 8, 8, [4096], 128, "f16", 0),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,d,dtype,splits", CASES,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_L{'-'.join(map(str, c[3]))}_d{c[4]}_{c[5]}_s{c[6]}" for c in CASES])
+def test_decode_matches_oracle(B, Hq, Hkv, lens, d, dtype, splits):
+    q, kc, vc, table, sl = si.make_decode_inputs(B, Hq, Hkv, lens, d, dtype, seed=3000 + sum(lens) + d, extra_blocks=5)
+    o, lse = check(q, kc, vc, table, sl, dtype, splits)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert (o[b] == 0).all() and torch.isneginf(lse[b]).all()
+
+
+def test_decode_ignores_garbage_past_sequence_end():
+    """Cache slots past each sequence's length hold NaN; they must not leak."""
+    B, Hq, Hkv, d = 3, 8, 2, 128
+    lens = [19, 40, 1]
+    q, kc, vc, table, sl = si.make_decode_inputs(B, Hq, Hkv, lens, d, "bf16", seed=91)
+    used = torch.zeros(kc.shape[0], 16, dtype=torch.bool)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            used[table[b, t // 16], t % 16] = True
+    unused = (~used)[:, None, :, None].expand_as(kc)  # cache is [pages, Hkv, slot, d]
+    kc[unused] = float("nan")
+    vc[unused] = float("nan")
+    o, lse = check(q, kc, vc, table, sl, "bf16")
+    assert torch.isfinite(o.float()).all()
+
+
+def test_decode_split_count_and_page_order_invariance():
+    B, Hq, Hkv, d = 2, 16, 4, 128
+    q, kc, vc, table, sl = si.make_decode_inputs(B, Hq, Hkv, [3000, 1234], d, "bf16", seed=17, extra_blocks=11)
+    sc = 1 / math.sqrt(d)
+    ref_o, ref_l = oracle_decode(q, kc, vc, table, sl, sc)
+    outs = []
+    for splits in (1, 7, 0, 64):
+        o, lse = run_decode(q, kc, vc, table, sl, sc, splits)
+        assert_close(f"O splits={splits}", f64(o), ref_o, "bf16", "o")
+        assert_close(f"LSE splits={splits}", f64(lse), ref_l, "bf16", "lse")
+        outs.append(o.float())
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max() <= 2e-2
+    # Move every page to another cache slot and rewrite the table accordingly.
+    perm = torch.randperm(kc.shape[0], generator=torch.Generator().manual_seed(5))
+    kc2, vc2 = torch.empty_like(kc), torch.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    table2 = perm[table.long()].to(torch.int32)
+    o2, l2 = run_decode(q, kc2, vc2, table2, sl, sc, 0)
+    o1, l1 = run_decode(q, kc, vc, table, sl, sc, 0)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_workload_gqa_paged_full():
+    w = si.WORKLOADS["decode_gqa_paged"]
+    q, kc, vc, table, sl = si.workload_decode_inputs(w)
+    o, lse = check(q, kc, vc, table, sl, w.dtype)
+    assert torch.isfinite(o.float()).all()
+
+
+def test_decode_bitwise_repeatable():
+    q, kc, vc, table, sl = si.make_decode_inputs(4, 32, 8, [5000, 17, 2000, 999], 128, "bf16", seed=23)
+    fa = _fa()
+    args = [dev(t) for t in (q, kc, vc, table, sl)]
+    o1, l1 = fa.decode_paged(*args)
+    o2, l2 = fa.decode_paged(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
