@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented codes before any HIP call.
+
+Fake device pointers here are deliberately 8-byte (not 16-byte) aligned, so a
+call whose other arguments were valid would still stop at FA_ERR_ALIGN: no
+test in this file can reach a kernel launch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, GQA, BLOCKSIZE, WORKSPACE, LAUNCH, SCALE, ALIGN = range(11)
+F32, F16, BF16 = 0, 1, 2
+P = 0x10008  # fake, misaligned device pointer
+NAN, INF = float("nan"), float("inf")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_io_aware_47_amd as pkg
+    from exact_io_aware_47_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_io_aware_47_amd import build
+        build.build()
+    return pkg
+
+
+@pytest.fixture(scope="module")
+def L(fa):
+    return fa.lib()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flash_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_decode_paged", "flash_attn_strerror",
+              "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    from exact_io_aware_47_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(declared_functions()) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_strerror(L):
+    for code in range(11):
+        s = L.flash_attn_strerror(code)
+        assert s and s != b"unknown error code"
+    assert L.flash_attn_strerror(123) == b"unknown error code"
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dtype=BF16):
+    return L.flash_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE), (dict(Nq=0), SHAPE), (dict(Nk=0), SHAPE),
+    (dict(d=96), HEADDIM), (dict(d=16), HEADDIM), (dict(d=256), HEADDIM),
+    (dict(Hq=6, Hkv=4), GQA),
+    (dict(B=1 << 16, Nq=1 << 16, d=128), SHAPE),
+    (dict(dtype=F32, Nq=1 << 22, d=128, B=1, Hq=1, Hkv=1), SHAPE),
+    (dict(scale=NAN), SCALE), (dict(scale=INF), SCALE),
+    (dict(), ALIGN), (dict(causal=1, dtype=F32), ALIGN),
+])
+def test_fwd_validation(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+def bwd(L, ws=P, ws_bytes=1 << 20, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125, dtype=F16, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(9)]
+    return L.flash_attn_bwd(*ptrs, B, Hq, Hkv, Nq, Nk, d, scale, 0, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nulls=(0,)), NULL), (dict(nulls=(4,)), NULL), (dict(nulls=(5,)), NULL), (dict(nulls=(8,)), NULL),
+    (dict(dtype=7), DTYPE), (dict(Nk=0), SHAPE), (dict(d=48), HEADDIM), (dict(Hq=3, Hkv=2), GQA),
+    (dict(scale=NAN), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=2 * 2 * 8 * 4 - 1), WORKSPACE),
+    (dict(ws_bytes=2 * 2 * 8 * 4), ALIGN),
+])
+def test_bwd_validation(L, kw, code):
+    assert bwd(L, **kw) == code
+
+
+def dec(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, bs=16, max_blocks=4,
+        nblocks=8, scale=0.1, splits=0, dtype=BF16, ws=P, ws_bytes=1 << 20):
+    return L.flash_attn_decode_paged(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, d, bs, max_blocks, nblocks, scale,
+                                     splits, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(table=None), NULL), (dict(lens=None), NULL), (dict(o=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(dtype=5), DTYPE),
+    (dict(B=0), SHAPE), (dict(max_blocks=0), SHAPE), (dict(nblocks=0), SHAPE), (dict(splits=-1), SHAPE),
+    (dict(d=80), HEADDIM), (dict(Hq=8, Hkv=3), GQA), (dict(bs=32), BLOCKSIZE), (dict(bs=8), BLOCKSIZE),
+    (dict(scale=INF), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(), ALIGN), (dict(lse=None), ALIGN),
+])
+def test_decode_validation(L, kw, code):
+    assert dec(L, **kw) == code
+
+
+def test_workspace_queries(L):
+    assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 128, BF16) == 2 * 2 * 16 * 4096 * 4
+    assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 96, BF16) == 0
+    # Automatic split count: about 4 work-groups per compute unit, at least 4 pages per split.
+    assert L.flash_attn_decode_num_splits(8, 8, 2048, 16) == 16
+    assert L.flash_attn_decode_num_splits(1, 1, 2, 16) == 1
+    assert L.flash_attn_decode_num_splits(1, 1, 100000, 16) == 1024
+    assert L.flash_attn_decode_num_splits(1, 8, 2048, 8) == 0
+    assert L.flash_attn_decode_workspace_bytes(8, 32, 8, 128, 2048, 16, 0) == 8 * 32 * 16 * (128 + 4) * 4
+    assert L.flash_attn_decode_workspace_bytes(8, 32, 8, 128, 2048, 16, 5) == 8 * 32 * 5 * (128 + 4) * 4
+    assert L.flash_attn_decode_workspace_bytes(8, 32, 8, 100, 2048, 16, 0) == 0
+
+
+def test_binding_refuses_host_tensors(fa):
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fa.fwd(q, q, q)
+
+
+def test_binding_maps_error_codes(fa, L):
+    err = fa.FlashAttnError(GQA, "flash_attn_fwd")
+    assert err.code == GQA and "FA_ERR_GQA" in str(err)
