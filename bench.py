@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X (gfx950).
+
+One step is the forward and the backward of exact causal attention on the
+bf16 training/prefill workload B=2, H=16, N=4096, d=128 (seeded synthetic
+N(0,1) inputs, resident in device memory before timing starts).  The
+backward is launched as its three phases (row terms, dK/dV, dQ) so that HIP
+events on the library's stream time every kernel of the step separately;
+the roofline object describes whichever kernel takes the most time.
+
+The same run also times the split-KV paged decode workload (B=8, Hq=32,
+Hkv=8, 32768 cached tokens per sequence, 16-token pages) against the HBM
+roof, and the float64 CPU oracle on a bounded sample of the training
+workload (its `cpu_baseline` leg; the only place this file touches the
+oracle).
+
+Prints one JSON line.  `--gpus` above 1 is refused: this build runs on a
+single GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16 = 2516.6  # TFLOP/s: 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM = 8000.0        # GB/s: MI355X HBM3E
+METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4096, d=128, causal) + % of MFMA peak"
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (what the method computes; the N x N work it avoids is not
+# counted).  Per visible (query, key) pair and head:
+#   forward   4d flops (S = QKᵀ and O = PV, 2 flops per multiply-add)
+#   dK/dV     8d flops (S recomputed, dP, dV, dK)
+#   dQ        2d flops (dQ; its own recomputation of S and dP is not counted)
+# so the backward is 10d = 2.5x the forward.
+# ---------------------------------------------------------------------------
+def visible_pairs(nq: int, nk: int, causal: bool) -> int:
+    if not causal:
+        return nq * nk
+    diag = nk - nq
+    # row i sees keys 0 .. i + diag (clipped to [0, nk])
+    total = 0
+    lo = max(0, -diag)              # first row that sees any key
+    full = max(lo, nk - diag)       # rows from here on see all nk keys
+    full = min(full, nq)
+    if full > lo:                   # rows lo..full-1 see i + diag + 1 keys
+        a, b = lo + diag + 1, full - 1 + diag + 1
+        total += (a + b) * (full - lo) // 2
+    total += (nq - full) * nk
+    return total
+
+
+def attention_flops(B, Hq, nq, nk, d, causal):
+    pairs = B * Hq * visible_pairs(nq, nk, causal)
+    return {"fwd": 4 * d * pairs, "dkdv": 8 * d * pairs, "dq": 2 * d * pairs}
+
+
+def prep_bytes(B, Hq, nq, d, es):
+    rows = B * Hq * nq
+    return rows * (2 * d * es + 4 + 2 * 4)  # read O, dO, LSE; write D and LSE*log2(e)
+
+
+def decode_bytes(B, Hq, Hkv, seq_len, d, es, block_size=16):
+    kv = 2 * B * Hkv * seq_len * d * es
+    pages = -(-seq_len // block_size)
+    return kv + 2 * B * Hq * d * es + B * Hq * 4 + B * pages * 4 + B * 4  # + Q, O, LSE, table, lengths
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_47_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "exact_io_aware_47_amd", "csrc", "fa_device.hpp"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"fwd": ("fa_fwd.hip",), "prep": ("fa_bwd.hip",), "dkdv": ("fa_bwd.hip",), "dq": ("fa_bwd.hip",),
+                  "decode": ("fa_decode.hip",)}
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(*KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def ensure_library():
+    from exact_io_aware_47_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_io_aware_47_amd import build
+        build.build()
+
+
+def bench_training(torch, fa, si, steps, warmup):
+    w = si.WORKLOADS["mha_bf16_4k"]
+    q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, fa.FA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    causal = True
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        if ev: ev[1].record()
+        fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, causal)
+        if ev: ev[2].record()
+        fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, causal)
+        if ev: ev[3].record()
+        fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, causal)
+        if ev: ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    names = ["fwd", "prep", "dkdv", "dq"]
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    return w, total_ms / steps, per, wall
+
+
+def bench_decode(torch, fa, si, steps, warmup):
+    w = si.WORKLOADS["decode_gqa_paged"]
+    q, kc, vc, table, lens = (t.to("cuda") for t in si.workload_decode_inputs(w))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.max_blocks), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        fa.decode_paged(q, kc, vc, table, lens, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fa.decode_paged(q, kc, vc, table, lens, out=out, lse=lse, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del kc, vc
+    return w, ms
+
+
+def cpu_baseline(si, budget_s: float):
+    """The float64 oracle, as it stands, on whole (batch, head) slices of the
+    training workload until about budget_s seconds of CPU work are done."""
+    import numpy as np
+    from oracle import attention_f64 as orc
+    w = si.WORKLOADS["mha_bf16_4k"]
+    q, k, v, do = si.workload_attention_inputs(w)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    if not threads:
+        threads = len(os.sched_getaffinity(0))
+    fl = attention_flops(1, 1, w.Nq, w.Nk, w.d, True)
+    per_head = fl["fwd"] + fl["dkdv"] + fl["dq"]
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.B * w.Hq:
+        b, h = divmod(heads, w.Hq)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        f = lambda t: t[sl].double().numpy()
+        orc.attention_fwd(f(q), f(k), f(v), w.scale, True)
+        orc.attention_bwd(f(q), f(k), f(v), f(do), w.scale, True)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(heads * per_head / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of mha_bf16_4k, causal forward + backward in "
+                      f"float64 numpy, {el:.1f} s; flops counted as for the GPU (visible pairs only)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention kernels here are "
+              "built and timed on a single MI355X and no multi-GPU path exists.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth_inputs as si
+    ensure_library()
+    import exact_io_aware_47_amd as fa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    props = torch.cuda.get_device_properties(0)
+
+    w, ms_step, per, wall = bench_training(torch, fa, si, args.steps, args.warmup)
+    fl = attention_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True)
+    step_flops = fl["fwd"] + fl["dkdv"] + fl["dq"]
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    work = {"fwd": ("mfma", fl["fwd"]), "prep": ("hbm", prep_bytes(w.B, w.Hq, w.Nq, w.d, 2)),
+            "dkdv": ("mfma", fl["dkdv"]), "dq": ("mfma", fl["dq"])}
+
+    def roofline(name, ms):
+        bound, amount = work[name]
+        if bound == "mfma":
+            ach, peak, unit = amount / (ms * 1e-3) / 1e12, PEAK_MFMA_BF16, "TFLOP/s"
+        else:
+            ach, peak, unit = amount / (ms * 1e-3) / 1e9, PEAK_HBM, "GB/s"
+        return {"kernel": name, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(name), "avg_us": round(ms * 1e3, 2)}
+
+    dominant = max(per, key=per.get)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mha_bf16_4k: causal attention forward + backward, bf16 in, fp32 accumulation",
+                   "B": w.B, "H": w.Hq, "N": w.Nq, "d": w.d, "causal": True, "seed": w.seed,
+                   "flops_per_step": step_flops},
+        "pct_mfma_peak": round(100 * value / PEAK_MFMA_BF16, 2),
+        "roofline": roofline(dominant, per[dominant]),
+        "kernels": {n: roofline(n, per[n]) for n in per},
+        "fwd_tflops": round(fl["fwd"] / (per["fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round((fl["dkdv"] + fl["dq"]) / ((per["prep"] + per["dkdv"] + per["dq"]) * 1e-3) / 1e12, 2),
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "host_wall_s_timed": round(wall, 4),
+    }
+    if not args.no_decode:
+        wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
+        nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)
+        gbs = nbytes / (ms_dec * 1e-3) / 1e9
+        line["decode"] = {"workload": "decode_gqa_paged: B=8 Hq=32 Hkv=8 Nk=32768 d=128 bf16, 16-token pages",
+                          "us": round(ms_dec * 1e3, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+                          "roofline": {"kernel": "decode (split + reduce)", "bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM, "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4),
+                                       "traffic": measured_traffic("decode")}}
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(si, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -35,6 +35,9 @@ SIGNATURES = {
     "flash_attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_bwd_preprocess": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "flash_attn_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -147,6 +150,31 @@ def bwd(q, k, v, out, dout, lse, causal: bool = False, scale=None, dq=None, dk=N
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "flash_attn_bwd")
     return dq, dk, dv
+
+
+def bwd_phase(phase: str, q, k, v, out, dout, lse, dq, dk, dv, workspace, causal: bool = False, scale=None):
+    """Run one backward phase ('preprocess', 'dkdv' or 'dq') on torch's current
+    stream; the outputs and the workspace are caller-allocated.  Arguments not
+    used by the phase may be None."""
+    ref = q if q is not None else out
+    B, Hq, Nq, d = ref.shape
+    Hkv, Nk = (k.shape[1], k.shape[2]) if k is not None else (Hq, Nq)
+    code_dt = _dtype_code(ref)
+    ws = (_ptr(workspace), workspace.numel() * workspace.element_size())
+    sc = _default_scale(d, scale)
+    L = lib()
+    if phase == "preprocess":
+        code = L.flash_attn_bwd_preprocess(_ptr(out), _ptr(dout), _ptr(lse), B, Hq, Nq, d, code_dt, *ws,
+                                           _stream(ref.device))
+    elif phase == "dkdv":
+        code = L.flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk,
+                                     d, sc, int(bool(causal)), code_dt, *ws, _stream(ref.device))
+    elif phase == "dq":
+        code = L.flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), B, Hq, Hkv, Nq, Nk, d, sc,
+                                   int(bool(causal)), code_dt, *ws, _stream(ref.device))
+    else:
+        raise ValueError(f"unknown backward phase {phase!r}")
+    _check(code, f"flash_attn_bwd_{phase}")
 
 
 def decode_num_splits(B, Hkv, max_blocks_per_seq, block_size=16) -> int:

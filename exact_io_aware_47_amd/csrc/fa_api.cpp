@@ -74,23 +74,69 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, in
   return 2 * (size_t)B * Hq * Nq * sizeof(float);  // D row terms, then LSE * log2(e)
 }
 
+}  // extern "C"
+
+namespace {
+
+// Everything a backward phase may touch; unused pointers are NULL.
+struct BwdPtrs {
+  const void *Q, *K, *V, *O, *dO;
+  const float* LSE;
+  void *dQ, *dK, *dV;
+  const void* workspace;
+};
+
+int run_bwd(const BwdPtrs& t, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+            size_t workspace_bytes, int phases, void* stream) {
+  const int st = check_dense(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!t.workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype))
+    return FA_ERR_WORKSPACE;
+  const void* dense[] = {t.Q, t.K, t.V, t.O, t.dO, t.dQ, t.dK, t.dV, t.workspace};
+  for (const void* p : dense)
+    if (p && !aligned(p, 16)) return FA_ERR_ALIGN;
+  if (t.LSE && !aligned(t.LSE, 4)) return FA_ERR_ALIGN;
+  fa::BwdArgs a;
+  a.q = t.Q; a.k = t.K; a.v = t.V; a.o = t.O; a.dout = t.dO; a.lse = t.LSE;
+  a.dq = t.dQ; a.dk = t.dK; a.dv = t.dV; a.dsum = (float*)t.workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  return launch_status(fa::launch_bwd(a, phases, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
 int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                    void* dQ, void* dK, void* dV, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                    int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
-  const int st = check_dense(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
-  if (st != FA_OK) return st;
-  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, dtype))
-    return FA_ERR_WORKSPACE;
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
-      !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4) || !aligned(workspace, 16))
-    return FA_ERR_ALIGN;
-  fa::BwdArgs a;
-  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
-  a.dq = dQ; a.dk = dK; a.dv = dV; a.dsum = (float*)workspace;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
-  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
-  return launch_status(fa::launch_bwd(a, (hipStream_t)stream));
+  const BwdPtrs t = {Q, K, V, O, dO, LSE, dQ, dK, dV, workspace};
+  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdAll, stream);
+}
+
+int flash_attn_bwd_preprocess(const void* O, const void* dO, const float* LSE, int B, int Hq, int Nq, int d,
+                              int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!O || !dO || !LSE) return FA_ERR_NULL;
+  const BwdPtrs t = {nullptr, nullptr, nullptr, O, dO, LSE, nullptr, nullptr, nullptr, workspace};
+  return run_bwd(t, B, Hq, Hq, Nq, Nq, d, 1.0f, 0, dtype, workspace_bytes, fa::kBwdPrep, stream);
+}
+
+int flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, void* dK, void* dV, int B,
+                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                        const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !dO || !dK || !dV) return FA_ERR_NULL;
+  const BwdPtrs t = {Q, K, V, nullptr, dO, nullptr, nullptr, dK, dV, workspace};
+  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdDkdv, stream);
+}
+
+int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, void* dQ, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, int dtype, const void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !dO || !dQ) return FA_ERR_NULL;
+  const BwdPtrs t = {Q, K, V, nullptr, dO, nullptr, dQ, nullptr, nullptr, workspace};
+  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdDq, stream);
 }
 
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {

@@ -413,63 +413,73 @@ void bwd_dq_kernel(DqParams p) {
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
-hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
+// Phase launchers.  The workspace holds D (rows floats) then lse2 (rows floats).
+template <typename T, int D>
+hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
-  float* dsum = a.dsum;
-  float* lse2 = a.dsum + rows;
-  {
-    constexpr int kTPR = D / (16 / (int)sizeof(T));
-    const int64_t threads = rows * kTPR;
-    const unsigned grid = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(grid), dim3(256), 0, stream, (const T*)a.o, (const T*)a.dout,
-                       a.lse, dsum, lse2, rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const float c = a.scale * kLog2e;
-  {
-    using C = DkvCfg<T, D>;
-    DkvParams p;
-    p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = lse2; p.dsum = dsum; p.dk = a.dk; p.dv = a.dv;
-    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-    p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
-    p.c = c; p.scale = a.scale;
-    const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    using C = DqCfg<T, D>;
-    DqParams p;
-    p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = lse2; p.dsum = dsum; p.dq = a.dq;
-    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-    p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
-    p.c = c; p.scale = a.scale;
-    const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
-  }
+  constexpr int kTPR = D / (16 / (int)sizeof(T));
+  const int64_t threads = rows * kTPR;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(grid), dim3(256), 0, stream, (const T*)a.o, (const T*)a.dout,
+                     a.lse, a.dsum, a.dsum + rows, rows);
   return hipGetLastError();
 }
 
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
+  using C = DkvCfg<T, D>;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  DkvParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = a.dsum + rows; p.dsum = a.dsum;
+  p.dk = a.dk; p.dv = a.dv;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
+  p.c = a.scale * kLog2e; p.scale = a.scale;
+  const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
+  using C = DqCfg<T, D>;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  DqParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = a.dsum + rows; p.dsum = a.dsum; p.dq = a.dq;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
+  p.c = a.scale * kLog2e; p.scale = a.scale;
+  const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_phases(const BwdArgs& a, int phases, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if ((phases & kBwdPrep) && (e = launch_prep<T, D>(a, stream)) != hipSuccess) return e;
+  if ((phases & kBwdDkdv) && (e = launch_dkdv<T, D, CAUSAL>(a, stream)) != hipSuccess) return e;
+  if ((phases & kBwdDq) && (e = launch_dq<T, D, CAUSAL>(a, stream)) != hipSuccess) return e;
+  return e;
+}
+
 template <typename T>
-hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_dtype(const BwdArgs& a, int phases, hipStream_t s) {
   switch (a.d) {
-    case 32: return a.causal ? launch_typed<T, 32, true>(a, s) : launch_typed<T, 32, false>(a, s);
-    case 64: return a.causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
-    case 128: return a.causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+    case 32: return a.causal ? launch_phases<T, 32, true>(a, phases, s) : launch_phases<T, 32, false>(a, phases, s);
+    case 64: return a.causal ? launch_phases<T, 64, true>(a, phases, s) : launch_phases<T, 64, false>(a, phases, s);
+    case 128: return a.causal ? launch_phases<T, 128, true>(a, phases, s) : launch_phases<T, 128, false>(a, phases, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream) {
   switch (a.dtype) {
-    case 0: return launch_dtype<float>(a, stream);
-    case 1: return launch_dtype<_Float16>(a, stream);
-    case 2: return launch_dtype<__bf16>(a, stream);
+    case 0: return launch_dtype<float>(a, phases, stream);
+    case 1: return launch_dtype<_Float16>(a, phases, stream);
+    case 2: return launch_dtype<__bf16>(a, phases, stream);
   }
   return hipErrorInvalidValue;
 }

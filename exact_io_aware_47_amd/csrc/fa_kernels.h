@@ -28,7 +28,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic, [B, Hq, Nq] float32
+  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic [B, Hq, Nq], then LSE_i*log2(e) [B, Hq, Nq]
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   bool causal;
@@ -43,14 +43,16 @@ struct DecodeArgs {
   const int* seq_lens;
   void* o;
   float* lse;  // may be null
-  float* part; // workspace: [B, Hq, splits, d + 2] float32
+  float* part; // workspace: [B, Hq, splits, d + 4] float32
   int B, Hq, Hkv, d, block_size, max_blocks, num_blocks, splits;
   float scale;
   int dtype;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// Backward phases (bit mask); kBwdAll runs them in order on one stream.
+constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
+hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -119,6 +119,29 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
                    int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward's three phases, for callers that schedule them themselves
+ * (flash_attn_bwd runs all three in this order on one stream):
+ *   1. flash_attn_bwd_preprocess writes the per-row terms D_i and
+ *      LSE_i*log2(e) into the workspace (reads O, dO, LSE);
+ *   2. flash_attn_bwd_dkdv writes dK, dV and flash_attn_bwd_dq writes dQ;
+ *      both read the workspace written by phase 1 and are independent of
+ *      each other, so they may run concurrently on two streams once phase 1
+ *      has completed.
+ * Arguments mean what they mean for flash_attn_bwd; the workspace must hold
+ * flash_attn_bwd_workspace_bytes(...) bytes.  Same error codes and order.
+ */
+int flash_attn_bwd_preprocess(const void* O, const void* dO, const float* LSE,
+                              int B, int Hq, int Nq, int d, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                        void* dK, void* dV,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        int dtype, const void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, void* dQ,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Number of KV splits the decode uses for num_splits = 0 (automatic): enough
  * work-groups to cover the 256 compute units several times over, with at
  * least 4 pages per split.  Pure host arithmetic, no HIP call.

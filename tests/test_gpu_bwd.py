@@ -115,3 +115,28 @@ def test_bwd_bitwise_repeatable():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_bwd_phases_on_two_streams_match_single_call():
+    """Preprocess, then dK/dV on the current stream and dQ on a second stream
+    concurrently: bitwise equal to flash_attn_bwd on one stream."""
+    fa = _fa()
+    q, k, v, do = si.make_attention_inputs(2, 8, 4, 513, 513, 64, "f16", seed=6)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.fwd(qd, kd, vd, causal=True)
+    ref = fa.bwd(qd, kd, vd, o, dod, lse, causal=True)
+    ws = torch.empty(fa.bwd_workspace_bytes(2, 8, 4, 513, 513, 64, fa.FA_F16), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    fa.bwd_phase("preprocess", None, None, None, o, dod, lse, None, None, None, ws, True)
+    ready = torch.cuda.Event()
+    ready.record(main)
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        fa.bwd_phase("dq", qd, kd, vd, None, dod, None, dq, None, None, ws, True)
+    fa.bwd_phase("dkdv", qd, kd, vd, None, dod, None, None, dk, dv, ws, True)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a, b)
