@@ -153,9 +153,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
       load_pair(pg0 + 2 * (i + 1), st ^ 1);
       // Wait for the older stage only: the newer pair's loads may stay in flight.
       // (A pair is 4 * kSlices loads; loads retire in issue order.)
-      if constexpr (C::kSlices == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if constexpr (C::kSlices == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      wait_vmem_le<4 * C::kSlices>();
     } else {
       wait_vmem();
     }
@@ -234,36 +232,48 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
   }
 }
 
+// One wave per (sequence, query head).  Lanes first reduce the splits' maxima
+// and sums in parallel (64 splits per round, fixed order, so the result is
+// deterministic), then each lane accumulates its d values over the splits.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, T* __restrict__ out,
                                                            float* __restrict__ lse, int splits) {
-  const int bh = blockIdx.x;
-  const float* rec = part + (size_t)bh * splits * (D + 4);
+  constexpr int kRec = D + 4;
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const float* rec = part + (size_t)bh * splits * kRec;
   float M = -INFINITY;
-  for (int s = 0; s < splits; s++) M = fmaxf(M, rec[(size_t)s * (D + 4) + D]);
+  for (int s = lane; s < splits; s += 64) M = fmaxf(M, rec[(size_t)s * kRec + D]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   float L = 0.f;
-  constexpr int kPer = D / 64 > 0 ? D / 64 : 1;
+  for (int s = lane; s < splits; s += 64) {
+    const float ms = rec[(size_t)s * kRec + D];
+    if (ms != -INFINITY) L = fmaf(rec[(size_t)s * kRec + D + 1], fast_exp2(ms - M), L);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+  constexpr int kPer = (D + 63) / 64;
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; j++) acc[j] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < splits; s++) {
-    const float* r = rec + (size_t)s * (D + 4);
+    const float* r = rec + (size_t)s * kRec;
     const float ms = r[D];
     const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-    L = fmaf(r[D + 1], wgt, L);
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
-      const int d = threadIdx.x + 64 * j;
+      const int d = lane + 64 * j;
       if (d < D) acc[j] = fmaf(r[d], wgt, acc[j]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
-    const int d = threadIdx.x + 64 * j;
+    const int d = lane + 64 * j;
     if (d < D) out[(size_t)bh * D + d] = (T)(acc[j] * inv);
   }
-  if (lse != nullptr && threadIdx.x == 0) lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+  if (lse != nullptr && lane == 0) lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D>

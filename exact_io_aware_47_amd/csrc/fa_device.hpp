@@ -137,7 +137,25 @@ __device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, off, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt through the compiler intrinsic (not inline asm), so that the
+// compiler's own wait insertion sees which loads have already been drained.
+// gfx9 encoding: vmcnt = bits [3:0] and [15:14], expcnt = [6:4], lgkmcnt = [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Work-group barrier that lets buffer-to-LDS loads stay in flight: only this
+// wave's LDS accesses are drained before s_barrier, and the "memory" clobber
+// keeps the compiler from moving memory accesses across it.  Code that needs
+// staged tiles to be visible calls wait_vmem() first.
+__device__ __forceinline__ void barrier_lds() {
+  wait_lds();
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // --------------------------------------------------------------------------
 // LDS tiles: rows of ROW_BYTES stored as 16-byte chunks whose position in a
@@ -177,10 +195,14 @@ template <int ROW_BYTES, int ROWS, int WAVES>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, uint32_t g0, lds_char* tile, int w, int lane) {
   using TT = Tile<ROW_BYTES>;
   constexpr int kSlices = ROWS * ROW_BYTES / 1024;
-  static_assert(kSlices * 1024 == ROWS * ROW_BYTES && kSlices % WAVES == 0, "tile must split into whole wave slices");
+  // With fewer slices than waves, the first kSlices waves move one each.
+  constexpr int kPer = kSlices >= WAVES ? kSlices / WAVES : 1;
+  constexpr int kActive = kSlices >= WAVES ? WAVES : kSlices;
+  static_assert(kSlices * 1024 == ROWS * ROW_BYTES && kPer * kActive == kSlices, "tile must split into whole wave slices");
+  if (kActive < WAVES && w >= kActive) return;
 #pragma unroll
-  for (int i = 0; i < kSlices / WAVES; i++) {
-    const int s0 = (w * (kSlices / WAVES) + i) * 64;
+  for (int i = 0; i < kPer; i++) {
+    const int s0 = (w * kPer + i) * 64;
     const int s = s0 + lane;
     const int row = s / TT::kChunks, pc = s % TT::kChunks;
     buf_load16_to_lds(r, g0 + row * ROW_BYTES + ((pc ^ TT::key(row)) << 4), tile + s0 * 16);
@@ -203,6 +225,26 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const lds_char* base, uint32_t of
 
 // sigma: swap bits 2 and 3 of a row index within a 32-row MFMA tile.
 __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// --------------------------------------------------------------------------
+// Instruction schedule of a block of LDS fragment reads feeding MFMAs: the
+// first PD MFMAs' reads are issued up front, then every MFMA is followed by
+// the reads of the MFMA PD places later, so each read has PD MFMA slots
+// (32 cycles each) to return.  NR reads, NM MFMAs, NR a multiple of NM.
+// --------------------------------------------------------------------------
+template <int NR, int NM, int PD>
+__device__ __forceinline__ void sched_reads_ahead() {
+  static_assert(NR % NM == 0 && PD <= NM, "reads per MFMA must be whole");
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  constexpr int r = NR / NM;
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, PD * r, 0);
+#pragma unroll
+  for (int i = 0; i < NM - PD; i++) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, r, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, PD, 0);
+}
 
 // --------------------------------------------------------------------------
 // Cross-lane helpers
@@ -279,6 +321,32 @@ struct Frags {
       for (int i = 0; i < 4; i++) { f.v[i] = as_float(a[i]); f.v[4 + i] = as_float(b[i]); }
       return f;
     }
+  }
+
+  // The same fragments from precomputed per-lane byte offsets (16-bit types):
+  // a row fragment is one 16-byte read, a column fragment two transposing reads.
+  __device__ static __forceinline__ Frag lds_row_at(const lds_char* base, uint32_t off) {
+    static_assert(kES == 2, "16-bit types only");
+    return __builtin_bit_cast(Frag, lds_read16(base, off));
+  }
+  __device__ static __forceinline__ Frag lds_col_at(const lds_char* base, uint32_t off0, uint32_t off1) {
+    static_assert(kES == 2, "16-bit types only");
+    const i16x4 a = lds_read_tr16(base, off0), b = lds_read_tr16(base, off1);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(Frag, c);
+  }
+  // Offsets used by lds_row(base, row, ks, h) and lds_col(base, r0 = 0, c0, lane)
+  // for a tile of TileT rows; adding 32*mt or 16*ps rows only adds a constant.
+  template <typename TileT>
+  __device__ static __forceinline__ uint32_t row_off(int row, int ks, int h) {
+    return TileT::off(row, 2 * ks + h);
+  }
+  template <typename TileT>
+  __device__ static __forceinline__ uint32_t col_off(int c0, int u, int lane) {
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int row = 8 * (lane >> 5) + 4 * u + ((lane & 15) >> 2);
+    return TileT::off(row, col >> 3) + ((col & 7) << 1);
   }
 
   // Store 4 consecutive elements (rounded to T) at byte offset `off`.

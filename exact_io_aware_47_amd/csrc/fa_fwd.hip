@@ -6,18 +6,30 @@
 // "Flash-Attention", section "Core idea": Q outer, K/V inner, running max /
 // sum / output, the N x N scores never leave the chip).
 //
-// Work decomposition (MI355X): one work-group of 4 waves owns 128 query rows
-// of one (batch, query head); each wave owns 32 of them, so no reduction ever
-// crosses waves.  The work-group streams the K/V head in tiles of kBC keys
-// through LDS (double-buffered, bounds-checked direct-to-LDS buffer loads).
-// Per tile each wave computes
-//   S^T = K_j Q^T            (kBC x 32, 32x32x16 MFMA, fp32 accumulation)
-//   online softmax in the log2 domain: one cross-lane max exchange per tile,
-//   P^T = exp2(S^T * scale*log2e - m)
-//   O^T = O^T * exp2(m_old - m_new) + V_j^T P^T   (P^T rounded to T, straight
-//                                                   from registers)
-// Lane l always holds query l % 32, so the running max/sum are per lane.
-// The final O = O^T / l and LSE = (m + log2 l) * ln 2 are written once.
+// Work decomposition (MI355X).  A work-group of 8 waves owns 256 query rows
+// of one (batch, query head); each wave owns 32 rows, so no reduction ever
+// crosses waves.  The K/V head streams through LDS in tiles of kBC keys
+// (bounds-checked buffer-to-LDS loads; K and V each double-buffered).  Per
+// tile j each wave computes
+//   Sᵀ = K_j Qᵀ                 (kBC x 32, 32x32x16 MFMA, fp32 accumulation)
+//   online softmax in the log2 domain, one cross-lane max exchange per tile,
+//   Pᵀ = exp2(Sᵀ * scale*log2e - m)
+//   Oᵀ = Oᵀ * exp2(m_old - m_new) + V_jᵀ Pᵀ   (Pᵀ rounded to T, straight from
+//                                              registers into the next MFMA)
+// Lane l always holds query l % 32, so the running max and sum are per lane;
+// O = Oᵀ / l and LSE = (m + log2 l) ln 2 are written once at the end.
+//
+// Matrix and vector work overlap by construction ("ping-pong"): waves 0-3
+// and 4-7 form two groups, and each SIMD holds one wave of each.  Time is cut
+// into slots separated by work-group barriers; in a slot one group runs its
+// matrix products (PV of tile j-1 and S of tile j) while the other runs the
+// softmax of its last S.  Group 1 runs one slot behind group 0, so every SIMD
+// always has one MFMA-phase wave and one VALU-phase wave.
+//
+// The running max moves only when a row's scores exceed it by more than 2^8
+// (conditional rescaling, named on the concept page "Flash-Attention" among
+// FlashAttention-4's techniques, "Known limits"); O and l share the stale max,
+// so the result is unchanged while most tiles skip the rescale.
 #include "fa_device.hpp"
 #include "fa_kernels.h"
 
@@ -26,17 +38,16 @@ namespace {
 
 template <typename T, int D>
 struct FwdCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kBR = 32 * kWaves;                    // query rows per work-group
   static constexpr int kES = Elem<T>::kBytes;
   static constexpr int kRowBytes = D * kES;
   static constexpr int kBC = (kES == 4 && D == 128) ? 32 : 64;  // keys per KV tile
   static constexpr int kKS = D / 16;                         // 16-wide k blocks along d
-  static constexpr int kMT = kBC / 32;                       // 32-key M tiles of S^T
-  static constexpr int kPS = kBC / 16;                       // 16-key k blocks of V^T P^T
-  static constexpr int kDT = D / 32;                         // 32-row M tiles of O^T
+  static constexpr int kMT = kBC / 32;                       // 32-key M tiles of Sᵀ
+  static constexpr int kPS = kBC / 16;                       // 16-key k blocks of Vᵀ Pᵀ
+  static constexpr int kDT = D / 32;                         // 32-row M tiles of Oᵀ
   static constexpr int kTileBytes = kBC * kRowBytes;
-  static constexpr int kLds = 2 * 2 * kTileBytes;            // {K, V} x double buffer
 };
 
 struct FwdParams {
@@ -50,17 +61,27 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
+constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
+
+template <int N> struct Int { static constexpr int value = N; };
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdParams p) {
   using C = FwdCfg<T, D>;
   using E = Elem<T>;
   using F = Frags<T>;
   using TT = Tile<C::kRowBytes>;
   typedef typename E::Frag Frag;
+  constexpr bool k16 = C::kES == 2;
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
-  lds_char* smem = (lds_char*)smem_raw;
+  // Four separate LDS objects (K and V, two buffers each): the compiler then
+  // knows that a tile being loaded never aliases the tiles being read, and
+  // does not make reads wait for the in-flight loads.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes], k_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes], v_lds1[C::kTileBytes];
+  auto kbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? k_lds1 : k_lds0); };
+  auto vbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? v_lds1 : v_lds0); };
 
   // Block -> (query tile, batch, head).  With the causal mask the last query
   // tiles carry the most work, so they are dispatched first.
@@ -74,9 +95,9 @@ void fwd_kernel(FwdParams p) {
   const int lane = lane_id(), w = wave_id();
   const int h = lane >> 5, col = lane & 31;
   const int q0 = qt * C::kBR;
-  const int qw = q0 + 32 * w;  // first query row of this wave
-  const int qrow = qw + col;   // this lane's query row
-  const int diag = p.Nk - p.Nq;  // key j is visible to row i iff j <= i + diag (causal)
+  const int qw = q0 + 32 * w;     // first query row of this wave
+  const int qrow = qw + col;      // this lane's query row
+  const int diag = p.Nk - p.Nq;   // key j is visible to row i iff j <= i + diag (causal)
 
   const size_t q_slab = (size_t)bh * p.Nq * D;
   const size_t kv_slab = ((size_t)b * p.Hkv + hkv) * p.Nk * D;
@@ -89,124 +110,183 @@ void fwd_kernel(FwdParams p) {
     const int last_key = min(q0 + C::kBR, p.Nq) - 1 + diag;
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
-
-  // Stage K/V tile j into LDS buffer `buf` (keys past Nk read as zero).
-  auto load_tile = [&](int j, int buf) {
-    lds_char* kb = smem + buf * 2 * C::kTileBytes;
-    const uint32_t g0 = (uint32_t)j * C::kBC * C::kRowBytes;
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, g0, kb, w, lane);
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, g0, kb + C::kTileBytes, w, lane);
+  auto dma_k = [&](int j, lds_char* dst) __attribute__((always_inline)) {
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
   };
+  auto dma_v = [&](int j, lds_char* dst) __attribute__((always_inline)) {
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  if (n_tiles > 0) dma_k(0, kbuf(0));
 
-  if (n_tiles > 0) load_tile(0, 0);
-
-  // Q^T as the B operand of S^T = K Q^T: lane holds row qrow, d = 16ks + 8h + 0..7.
+  // Qᵀ as the B operand of Sᵀ = K Qᵀ: lane holds row qrow, d = 16ks + 8h + 0..7.
   Frag qf[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ks++) qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
 
+  // Per-lane LDS offsets of the K row fragments (A rows are sigma-permuted
+  // keys) and of the V column fragments; M tiles / k blocks add constants.
+  uint32_t koff[k16 ? C::kKS : 1], voff[k16 ? C::kDT : 1][2];
+  if constexpr (k16) {
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ks++) koff[ks] = F::template row_off<TT>(sigma(col), ks, h);
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; dt++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) voff[dt][u] = F::template col_off<TT>(32 * dt, u, lane);
+  }
+
   f32x16 o[C::kDT];
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++) o[dt] = f32x16{};
-  float m = -INFINITY;  // running max of scale*log2e*s (log2 domain)
+  f32x16 s[C::kMT];     // scores of the last S, consumed by the next softmax
+  Frag pf[C::kPS];      // probabilities of the last softmax, consumed by the next PV
+  float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
   float l = 0.f;        // this lane's share of the running sum (the other half-wave holds the rest)
   const bool fast_ok = p.c > 0.f;
 
-  wait_vmem();
-  __syncthreads();
+  // Does this wave see any key of tile j?
+  auto active = [&](int j) __attribute__((always_inline)) { return j < n_tiles && (!CAUSAL || j * C::kBC <= qw + 31 + diag); };
 
-  for (int j = 0; j < n_tiles; j++) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1, buf ^ 1);
-    const lds_char* kb = smem + buf * 2 * C::kTileBytes;
-    const lds_char* vb = kb + C::kTileBytes;
+  // ---- the three phases --------------------------------------------------
+  auto gemm_s = [&](const lds_char* kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++) s[mt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ks++) {
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++) {
+        Frag a;
+        if constexpr (k16) a = F::lds_row_at(kb + 32 * mt * C::kRowBytes, koff[ks]);
+        else a = F::template lds_row<TT>(kb, 32 * mt + sigma(col), ks, h);
+        s[mt] = E::mma(a, qf[ks], s[mt]);
+      }
+    }
+    if constexpr (k16) sched_reads_ahead<C::kKS * C::kMT, C::kKS * C::kMT, 4>();
+  };
+  auto gemm_pv = [&](const lds_char* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ps = 0; ps < C::kPS; ps++) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; dt++) {
+        Frag a;
+        if constexpr (k16) a = F::lds_col_at(vb + 16 * ps * C::kRowBytes, voff[dt][0], voff[dt][1]);
+        else a = F::template lds_col<TT>(vb, 16 * ps, 32 * dt, lane);
+        o[dt] = E::mma(a, pf[ps], o[dt]);
+      }
+    }
+    if constexpr (k16) sched_reads_ahead<2 * C::kPS * C::kDT, C::kPS * C::kDT, 4>();
+  };
+  // Register r of M tile mt holds key k0 + 32*mt + 16*(r/8) + 8h + (r%8).
+  auto softmax = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * C::kBC;
-
-    // A wave whose rows all end before this tile skips it (it still joins the barrier).
-    if (!CAUSAL || k0 <= qw + 31 + diag) {
-      // ---- S^T = K_j Q^T; A rows are sigma-permuted keys.
-      f32x16 s[C::kMT];
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++) s[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::kKS; ks++) {
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++) {
-          const Frag a = F::template lds_row<TT>(kb, 32 * mt + sigma(col), ks, h);
-          s[mt] = E::mma(a, qf[ks], s[mt]);
-        }
-      }
-
-      // ---- online softmax.  Register r of M tile mt holds key
-      //      k0 + 32*mt + 16*(r/8) + 8h + (r%8) for query qrow.
-      const bool need_mask = !fast_ok || (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
-      float m_new, m_use;
-      if (!need_mask) {
-        float mx = s[0][0];
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[mt][r]);
-        mx = fmaxf(mx, xor32(mx));
-        m_new = fmaxf(m, mx * p.c);
-        m_use = m_new;
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(fmaf(s[mt][r], p.c, -m_use));
-      } else {
-        float mx = -INFINITY;
-        const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int key = k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7);
-            const float t = key <= horizon ? s[mt][r] * p.c : -INFINITY;
-            s[mt][r] = t;
-            mx = fmaxf(mx, t);
-          }
-        mx = fmaxf(mx, xor32(mx));
-        m_new = fmaxf(m, mx);
-        m_use = m_new == -INFINITY ? 0.f : m_new;
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(s[mt][r] - m_use);
-      }
-      const float alpha = fast_exp2(m - m_use);  // 0 on the first visible tile
-      m = m_new;
-      float rs = 0.f;
+    const bool need_mask = !fast_ok || (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
+    float mx;
+    if (!need_mask) {
+      mx = s[0][0];
 #pragma unroll
       for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) rs += s[mt][r];
-      l = l * alpha + rs;
-      if (!__all(alpha == 1.f)) {
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[mt][r]);
+      mx = fmaxf(mx, xor32(mx)) * p.c;
+    } else {
+      mx = -INFINITY;
+      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
 #pragma unroll
-        for (int dt = 0; dt < C::kDT; dt++) o[dt] *= alpha;
-      }
-
-      // ---- O^T += V_j^T P^T.  P^T k block ps = registers 8*(ps%2).. of tile ps/2.
+      for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int ps = 0; ps < C::kPS; ps++) {
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; t++) pv[t] = s[ps >> 1][8 * (ps & 1) + t];
-        const Frag pf = E::pack(pv);
-#pragma unroll
-        for (int dt = 0; dt < C::kDT; dt++) {
-          const Frag a = F::template lds_col<TT>(vb, 16 * ps, 32 * dt, lane);
-          o[dt] = E::mma(a, pf, o[dt]);
+        for (int r = 0; r < 16; r++) {
+          const int key = k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7);
+          const float t = key <= horizon ? s[mt][r] * p.c : -INFINITY;
+          s[mt][r] = t;
+          mx = fmaxf(mx, t);
         }
+      mx = fmaxf(mx, xor32(mx));
+    }
+    // Move the running max only if it grows by more than kTau.
+    const bool grow = mx > m + kTau;
+    if (__any(grow)) {
+      // 1 where the max stays (also rows that have seen no key yet), 0 on a row's first keys.
+      const float alpha = grow ? fast_exp2(m - mx) : 1.f;
+      m = grow ? mx : m;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; dt++) o[dt] *= alpha;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;  // rows that have seen no key yet
+    if (!need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(fmaf(s[mt][r], p.c, -m_use));
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(s[mt][r] - m_use);
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) rs += s[mt][r];
+    l += rs;
+    // Pᵀ k block ps = registers 8*(ps%2).. of tile ps/2.
+#pragma unroll
+    for (int ps = 0; ps < C::kPS; ps++) {
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 8; t++) pv[t] = s[ps >> 1][8 * (ps & 1) + t];
+      pf[ps] = E::pack(pv);
+    }
+  };
+
+  // ---- slot schedule -----------------------------------------------------
+  // Slot t (one barrier after each): loads of K(t/2 + 1) and V(t/2) are issued
+  // in even slots and waited for at the end of the next (odd) slot.  A wave
+  // of group G runs phase u = t - G: even u = GEMM of tile u/2 (PV of tile
+  // u/2 - 1, then S of tile u/2), odd u = softmax of tile (u-1)/2.  Slots
+  // are unrolled by 4 so every buffer parity is a compile-time constant.
+  const int G = w >> 2;
+  const int n_slots = (2 * n_tiles + 2 + 3) & ~3;
+
+  auto slot = [&](auto gc, auto pc, int t) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value, p4 = decltype(pc)::value;
+    if constexpr ((p4 & 1) == 0) {
+      const int j = t >> 1;
+      constexpr int jp = (p4 >> 1) & 1;  // parity of j
+      if (j + 1 < n_tiles) dma_k(j + 1, kbuf(jp ^ 1));
+      if (j < n_tiles) dma_v(j, vbuf(jp));
+    }
+    const int u = t - g;
+    if (u >= 0) {
+      if constexpr (((p4 - g) & 1) == 0) {
+        const int j = u >> 1;
+        constexpr int jp = ((p4 - g + 4) >> 1) & 1;  // parity of j
+        if (j >= 1 && active(j - 1)) gemm_pv(vbuf(jp ^ 1));
+        if (active(j)) gemm_s(kbuf(jp));
+      } else {
+        const int j = (u - 1) >> 1;
+        if (active(j)) softmax(j);
       }
     }
+    if constexpr (p4 & 1) wait_vmem();
+    barrier_lds();
+  };
 
-    wait_vmem();
-    __syncthreads();
-  }
+  wait_vmem();
+  barrier_lds();
+  auto run = [&](auto gc) __attribute__((always_inline)) {
+    for (int t = 0; t < n_slots; t += 4) {
+      slot(gc, Int<0>{}, t);
+      slot(gc, Int<1>{}, t + 1);
+      slot(gc, Int<2>{}, t + 2);
+      slot(gc, Int<3>{}, t + 3);
+    }
+  };
+  if (G == 0) run(Int<0>{});
+  else run(Int<1>{});
 
-  // ---- epilogue: O = O^T / l, LSE = m + log2(l) in natural log.
+  // ---- epilogue: O = Oᵀ / l, LSE = m + log2(l) in natural log.
   const float lt = l + xor32(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
@@ -234,7 +314,7 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
