@@ -76,8 +76,6 @@ struct DkvCfg {
   static constexpr int kDT = D / 32;
   static constexpr int kTileBytes = kBQ * kRowBytes;
   static constexpr int kStatBytes = 2 * kBQ * 4;  // lse2, dsum of the step's rows
-  static constexpr int kBufBytes = 2 * kTileBytes + kStatBytes;
-  static constexpr int kLds = 2 * kBufBytes;
   static_assert(kStatBytes == 512, "stats are staged by 32 lanes x 16 B");
 };
 
@@ -112,8 +110,15 @@ void bwd_dkdv_kernel(DkvParams p) {
   using TT = Tile<C::kRowBytes>;
   typedef typename E::Frag Frag;
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
-  lds_char* smem = (lds_char*)smem_raw;
+  // Double-buffered Q, dO and stats tiles, each buffer its own LDS object: the
+  // compiler then knows that the tiles being loaded never alias the tiles
+  // being read, and does not make the reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) char q_lds0[C::kTileBytes], q_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char do_lds0[C::kTileBytes], do_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(512))) char st_lds0[C::kStatBytes], st_lds1[C::kStatBytes];
+  auto qbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? q_lds1 : q_lds0); };
+  auto dobuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? do_lds1 : do_lds0); };
+  auto stbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? st_lds1 : st_lds0); };
 
   // Block -> (key tile, batch, kv head).  Under the causal mask the first key
   // tiles are seen by the most query rows, so they go first.
@@ -141,22 +146,22 @@ void bwd_dkdv_kernel(DkvParams p) {
   const int per_head = n_qt - qt0;
   const int steps = g * per_head;
 
-  auto load_step = [&](int s, int buf) {
+  auto load_step = [&](int s, int buf) __attribute__((always_inline)) {
     const int hq = hkv * g + s / per_head;
     const int qt = qt0 + s % per_head;
     const size_t bhq = (size_t)b * p.Hq + hq;
     const size_t q_slab = bhq * p.Nq * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
-    lds_char* qb = smem + buf * C::kBufBytes;
     const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
-    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, qb, w, lane);
-    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, qb + C::kTileBytes, w, lane);
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, buf ? qbuf(1) : qbuf(0), w, lane);
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, buf ? dobuf(1) : dobuf(0), w, lane);
     // Per-row stats of the step: lanes 0-15 stage lse2, lanes 16-31 dsum.
     if (w == 0) {
       const uint32_t off = (uint32_t)qt * C::kBQ * 4 + (lane & 15) * 16;
-      if (lane < 16) buf_load16_to_lds(make_rsrc(p.lse2 + bhq * p.Nq, (uint32_t)p.Nq * 4), off, qb + 2 * C::kTileBytes);
-      else if (lane < 32) buf_load16_to_lds(make_rsrc(p.dsum + bhq * p.Nq, (uint32_t)p.Nq * 4), off, qb + 2 * C::kTileBytes);
+      lds_char* st = buf ? stbuf(1) : stbuf(0);
+      if (lane < 16) buf_load16_to_lds(make_rsrc(p.lse2 + bhq * p.Nq, (uint32_t)p.Nq * 4), off, st);
+      else if (lane < 32) buf_load16_to_lds(make_rsrc(p.dsum + bhq * p.Nq, (uint32_t)p.Nq * 4), off, st);
     }
   };
 
@@ -173,67 +178,105 @@ void bwd_dkdv_kernel(DkvParams p) {
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
 
+  // Per-lane LDS offsets of the Q / dO row fragments (A rows are sigma-permuted
+  // queries) and of the Qᵀ / dOᵀ column fragments.
+  uint32_t roff[C::kKS], coff[C::kDT][2];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ks++) roff[ks] = F::template row_off<TT>(sigma(col), ks, h);
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++)
+#pragma unroll
+    for (int u = 0; u < 2; u++) coff[dt][u] = F::template col_off<TT>(32 * dt, u, lane);
+
   wait_vmem();
-  __syncthreads();
+  barrier_lds();
 
-  for (int s = 0; s < steps; s++) {
-    const int buf = s & 1;
-    if (s + 1 < steps) load_step(s + 1, buf ^ 1);
-    const lds_char* qb = smem + buf * C::kBufBytes;
-    const lds_char* dob = qb + C::kTileBytes;
-    const lds_char* stb = qb + 2 * C::kTileBytes;
+  // One step: query rows i0 .. i0 + kBQ - 1 of one query head.
+  auto step = [&](int s, const lds_char* qb, const lds_char* dob, const lds_char* stb) __attribute__((always_inline)) {
     const int i0 = (qt0 + s % per_head) * C::kBQ;  // first query row of the step
-
-    if (!CAUSAL || i0 + C::kBQ - 1 + diag >= kw) {
-      // ---- S = Q Kᵀ and dP = dO Vᵀ; A rows are sigma-permuted queries.
-      f32x16 sv[C::kMT], dp[C::kMT];
+    if (CAUSAL && i0 + C::kBQ - 1 + diag < kw) return;
+    // ---- S = Q Kᵀ and dP = dO Vᵀ; A rows are sigma-permuted queries.
+    f32x16 sv[C::kMT], dp[C::kMT];
 #pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+    for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ks++) {
+    for (int ks = 0; ks < C::kKS; ks++) {
 #pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++) {
+      for (int mt = 0; mt < C::kMT; mt++) {
+        if constexpr (C::kES == 2) {
+          sv[mt] = E::mma(F::lds_row_at(qb + 32 * mt * C::kRowBytes, roff[ks]), kf[ks], sv[mt]);
+          dp[mt] = E::mma(F::lds_row_at(dob + 32 * mt * C::kRowBytes, roff[ks]), vf[ks], dp[mt]);
+        } else {
           const int row = 32 * mt + sigma(col);
           sv[mt] = E::mma(F::template lds_row<TT>(qb, row, ks, h), kf[ks], sv[mt]);
           dp[mt] = E::mma(F::template lds_row<TT>(dob, row, ks, h), vf[ks], dp[mt]);
         }
       }
-      // ---- P and dS.  Register r of M tile mt holds query
-      //      i0 + 32*mt + 16*(r/8) + 8h + (r%8) for this lane's key.
-      const bool need_mask = CAUSAL && kw + 31 > i0 + diag;
+    }
+    if constexpr (C::kES == 2) sched_reads_ahead<2 * C::kKS * C::kMT, 2 * C::kKS * C::kMT, 4>();
+    // ---- P and dS.  Register r of M tile mt holds query
+    //      i0 + 32*mt + 16*(r/8) + 8h + (r%8) for this lane's key.
+    const bool need_mask = CAUSAL && kw + 31 > i0 + diag;
 #pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++)
+    for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          float l2[8], dd[8];
-          lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
-          lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
+      for (int u = 0; u < 2; u++) {
+        float l2[8], dd[8];
+        lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
+        lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
 #pragma unroll
-          for (int t = 0; t < 8; t++) {
-            const int r = 8 * u + t;
-            float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2[t]));
-            if (need_mask && key > i0 + 32 * mt + 16 * u + 8 * h + t + diag) pr = 0.f;
-            sv[mt][r] = pr;
-            dp[mt][r] = pr * (dp[mt][r] - dd[t]);
-          }
+        for (int t = 0; t < 8; t++) {
+          const int r = 8 * u + t;
+          float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2[t]));
+          if (need_mask && key > i0 + 32 * mt + 16 * u + 8 * h + t + diag) pr = 0.f;
+          sv[mt][r] = pr;
+          dp[mt][r] = pr * (dp[mt][r] - dd[t]);
         }
-      // ---- dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (column = key, k = query).
+      }
+    // ---- dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (column = key, k = query).
 #pragma unroll
-      for (int ps = 0; ps < C::kPS; ps++) {
-        float pv[8], dsv[8];
+    for (int ps = 0; ps < C::kPS; ps++) {
+      float pv[8], dsv[8];
 #pragma unroll
-        for (int t = 0; t < 8; t++) { pv[t] = sv[ps >> 1][8 * (ps & 1) + t]; dsv[t] = dp[ps >> 1][8 * (ps & 1) + t]; }
-        const Frag pf = E::pack(pv), dsf = E::pack(dsv);
+      for (int t = 0; t < 8; t++) { pv[t] = sv[ps >> 1][8 * (ps & 1) + t]; dsv[t] = dp[ps >> 1][8 * (ps & 1) + t]; }
+      const Frag pf = E::pack(pv), dsf = E::pack(dsv);
 #pragma unroll
-        for (int dt = 0; dt < C::kDT; dt++) {
+      for (int dt = 0; dt < C::kDT; dt++) {
+        if constexpr (C::kES == 2) {
+          dv[dt] = E::mma(F::lds_col_at(dob + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]), pf, dv[dt]);
+          dk[dt] = E::mma(F::lds_col_at(qb + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]), dsf, dk[dt]);
+        } else {
           dv[dt] = E::mma(F::template lds_col<TT>(dob, 16 * ps, 32 * dt, lane), pf, dv[dt]);
           dk[dt] = E::mma(F::template lds_col<TT>(qb, 16 * ps, 32 * dt, lane), dsf, dk[dt]);
         }
       }
     }
+    if constexpr (C::kES == 2) sched_reads_ahead<4 * C::kPS * C::kDT, 2 * C::kPS * C::kDT, 4>();
+  };
 
-    wait_vmem();
-    __syncthreads();
+  if constexpr (C::kES == 2) {
+    // Two steps per trip so that every buffer is a compile-time LDS object.
+    for (int s = 0; s < steps; s += 2) {
+      if (s + 1 < steps) load_step(s + 1, 1);
+      step(s, qbuf(0), dobuf(0), stbuf(0));
+      wait_vmem();
+      barrier_lds();
+      if (s + 1 < steps) {
+        if (s + 2 < steps) load_step(s + 2, 0);
+        step(s + 1, qbuf(1), dobuf(1), stbuf(1));
+        wait_vmem();
+        barrier_lds();
+      }
+    }
+  } else {
+    // float32: one step per trip (its larger fragments leave no room to unroll).
+    for (int s = 0; s < steps; s++) {
+      const int buf = s & 1;
+      if (s + 1 < steps) load_step(s + 1, buf ^ 1);
+      step(s, qbuf(buf), dobuf(buf), stbuf(buf));
+      wait_vmem();
+      barrier_lds();
+    }
   }
 
   // ---- epilogue: dK = scale * dKᵀ acc, dV; lane's column is its key.
@@ -265,7 +308,6 @@ struct DqCfg {
   static constexpr int kPS = kBC / 16;
   static constexpr int kDT = D / 32;
   static constexpr int kTileBytes = kBC * kRowBytes;
-  static constexpr int kLds = 2 * 2 * kTileBytes;
 };
 
 struct DqParams {
@@ -291,8 +333,11 @@ void bwd_dq_kernel(DqParams p) {
   using TT = Tile<C::kRowBytes>;
   typedef typename E::Frag Frag;
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
-  lds_char* smem = (lds_char*)smem_raw;
+  // Double-buffered K and V tiles, each buffer its own LDS object.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes], k_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes], v_lds1[C::kTileBytes];
+  auto kbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? k_lds1 : k_lds0); };
+  auto vbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? v_lds1 : v_lds0); };
 
   const int bh_count = p.B * p.Hq;
   const int id = blockIdx.x;
@@ -323,11 +368,10 @@ void bwd_dq_kernel(DqParams p) {
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
 
-  auto load_tile = [&](int j, int buf) {
-    lds_char* kb = smem + buf * 2 * C::kTileBytes;
+  auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
     const uint32_t g0 = (uint32_t)j * C::kBC * C::kRowBytes;
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, g0, kb, w, lane);
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, g0, kb + C::kTileBytes, w, lane);
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, g0, buf ? kbuf(1) : kbuf(0), w, lane);
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, g0, buf ? vbuf(1) : vbuf(0), w, lane);
   };
 
   if (n_tiles > 0) load_tile(0, 0);
@@ -345,58 +389,94 @@ void bwd_dq_kernel(DqParams p) {
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++) dq[dt] = f32x16{};
 
+  // Per-lane LDS offsets of the K / V row fragments (A rows are sigma-permuted
+  // keys) and of the Kᵀ column fragments.
+  uint32_t roff[C::kKS], coff[C::kDT][2];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ks++) roff[ks] = F::template row_off<TT>(sigma(col), ks, h);
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; dt++)
+#pragma unroll
+    for (int u = 0; u < 2; u++) coff[dt][u] = F::template col_off<TT>(32 * dt, u, lane);
+
   wait_vmem();
-  __syncthreads();
+  barrier_lds();
 
-  for (int j = 0; j < n_tiles; j++) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1, buf ^ 1);
-    const lds_char* kb = smem + buf * 2 * C::kTileBytes;
-    const lds_char* vb = kb + C::kTileBytes;
+  auto tile = [&](int j, const lds_char* kb, const lds_char* vb) __attribute__((always_inline)) {
     const int k0 = j * C::kBC;
-
-    if (!CAUSAL || k0 <= qw + 31 + diag) {
-      // ---- Sᵀ = K Qᵀ and dPᵀ = V dOᵀ; A rows are sigma-permuted keys.
-      f32x16 sv[C::kMT], dp[C::kMT];
+    if (CAUSAL && k0 > qw + 31 + diag) return;
+    // ---- Sᵀ = K Qᵀ and dPᵀ = V dOᵀ; A rows are sigma-permuted keys.
+    f32x16 sv[C::kMT], dp[C::kMT];
 #pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+    for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ks++) {
+    for (int ks = 0; ks < C::kKS; ks++) {
 #pragma unroll
-        for (int mt = 0; mt < C::kMT; mt++) {
+      for (int mt = 0; mt < C::kMT; mt++) {
+        if constexpr (C::kES == 2) {
+          sv[mt] = E::mma(F::lds_row_at(kb + 32 * mt * C::kRowBytes, roff[ks]), qf[ks], sv[mt]);
+          dp[mt] = E::mma(F::lds_row_at(vb + 32 * mt * C::kRowBytes, roff[ks]), dof[ks], dp[mt]);
+        } else {
           const int row = 32 * mt + sigma(col);
           sv[mt] = E::mma(F::template lds_row<TT>(kb, row, ks, h), qf[ks], sv[mt]);
           dp[mt] = E::mma(F::template lds_row<TT>(vb, row, ks, h), dof[ks], dp[mt]);
         }
       }
-      // ---- dSᵀ = Pᵀ ∘ (dPᵀ - D).  Register r of tile mt holds key
-      //      k0 + 32*mt + 16*(r/8) + 8h + (r%8).  Keys past Nk are masked too
-      //      (their zero-filled rows must not meet an infinite P).
-      const bool need_mask = (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
-      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
+    }
+    if constexpr (C::kES == 2) sched_reads_ahead<2 * C::kKS * C::kMT, 2 * C::kKS * C::kMT, 4>();
+    // ---- dSᵀ = Pᵀ ∘ (dPᵀ - D).  Register r of tile mt holds key
+    //      k0 + 32*mt + 16*(r/8) + 8h + (r%8).  Keys past Nk are masked too
+    //      (their zero-filled rows must not meet an infinite P).
+    const bool need_mask = (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
+    const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
 #pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++)
+    for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
-          if (need_mask && k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) > horizon) pr = 0.f;
-          dp[mt][r] = pr * (dp[mt][r] - dd);
-        }
-      // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
+      for (int r = 0; r < 16; r++) {
+        float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
+        if (need_mask && k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) > horizon) pr = 0.f;
+        dp[mt][r] = pr * (dp[mt][r] - dd);
+      }
+    // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
 #pragma unroll
-      for (int ps = 0; ps < C::kPS; ps++) {
-        float dsv[8];
+    for (int ps = 0; ps < C::kPS; ps++) {
+      float dsv[8];
 #pragma unroll
-        for (int t = 0; t < 8; t++) dsv[t] = dp[ps >> 1][8 * (ps & 1) + t];
-        const Frag dsf = E::pack(dsv);
+      for (int t = 0; t < 8; t++) dsv[t] = dp[ps >> 1][8 * (ps & 1) + t];
+      const Frag dsf = E::pack(dsv);
 #pragma unroll
-        for (int dt = 0; dt < C::kDT; dt++)
+      for (int dt = 0; dt < C::kDT; dt++) {
+        if constexpr (C::kES == 2)
+          dq[dt] = E::mma(F::lds_col_at(kb + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]), dsf, dq[dt]);
+        else
           dq[dt] = E::mma(F::template lds_col<TT>(kb, 16 * ps, 32 * dt, lane), dsf, dq[dt]);
       }
     }
+    if constexpr (C::kES == 2) sched_reads_ahead<2 * C::kPS * C::kDT, C::kPS * C::kDT, 4>();
+  };
 
-    wait_vmem();
-    __syncthreads();
+  if constexpr (C::kES == 2) {
+    // Two tiles per trip so that every buffer is a compile-time LDS object.
+    for (int j = 0; j < n_tiles; j += 2) {
+      if (j + 1 < n_tiles) load_tile(j + 1, 1);
+      tile(j, kbuf(0), vbuf(0));
+      wait_vmem();
+      barrier_lds();
+      if (j + 1 < n_tiles) {
+        if (j + 2 < n_tiles) load_tile(j + 2, 0);
+        tile(j + 1, kbuf(1), vbuf(1));
+        wait_vmem();
+        barrier_lds();
+      }
+    }
+  } else {
+    for (int j = 0; j < n_tiles; j++) {
+      const int buf = j & 1;
+      if (j + 1 < n_tiles) load_tile(j + 1, buf ^ 1);
+      tile(j, kbuf(buf), vbuf(buf));
+      wait_vmem();
+      barrier_lds();
+    }
   }
 
   const __amdgpu_buffer_rsrc_t wq = make_rsrc((char*)p.dq + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
