@@ -234,22 +234,38 @@ __device__ __forceinline__ int sigma(int r) { return (r & ~12) | ((r & 4) << 1) 
 // --------------------------------------------------------------------------
 template <int NR, int NM, int PD>
 __device__ __forceinline__ void sched_reads_ahead() {
-  static_assert(NR % NM == 0 && PD <= NM, "reads per MFMA must be whole");
+  static_assert(NR % NM == 0, "reads per MFMA must be whole");
   constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
   constexpr int r = NR / NM;
-  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, PD * r, 0);
+  constexpr int pd = PD < NM ? PD : NM;  // short blocks: all reads up front
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, pd * r, 0);
 #pragma unroll
-  for (int i = 0; i < NM - PD; i++) {
+  for (int i = 0; i < NM - pd; i++) {
     __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kMaskDsRead, r, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kMaskMfma, PD, 0);
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, pd, 0);
 }
 
 // --------------------------------------------------------------------------
 // Cross-lane helpers
 // --------------------------------------------------------------------------
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(x, x of the lane 32 places away) in every lane, on the VALU
+// (v_permlane32_swap exchanges the upper half of one operand with the lower
+// half of the other; with both operands x the two results hold x's lower and
+// upper halves in both halves).
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(as_float((uint32_t)r[0]), as_float((uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return as_float((uint32_t)r[0]) + as_float((uint32_t)r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

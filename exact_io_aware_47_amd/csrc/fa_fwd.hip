@@ -182,12 +182,16 @@ void fwd_kernel(FwdParams p) {
     const bool need_mask = !fast_ok || (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
     float mx;
     if (!need_mask) {
-      mx = s[0][0];
+      // Four independent three-input max chains.
+      float x[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
       for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[mt][r]);
-      mx = fmaxf(mx, xor32(mx)) * p.c;
+        for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
+      mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * p.c;
     } else {
       mx = -INFINITY;
       const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
@@ -200,7 +204,7 @@ void fwd_kernel(FwdParams p) {
           s[mt][r] = t;
           mx = fmaxf(mx, t);
         }
-      mx = fmaxf(mx, xor32(mx));
+      mx = max_halves(mx);
     }
     // Move the running max only if it grows by more than kTau.
     const bool grow = mx > m + kTau;
@@ -224,12 +228,12 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(s[mt][r] - m_use);
     }
-    float rs = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) rs += s[mt][r];
-    l += rs;
+      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     // Pᵀ k block ps = registers 8*(ps%2).. of tile ps/2.
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
@@ -269,8 +273,13 @@ void fwd_kernel(FwdParams p) {
         if (active(j)) softmax(j);
       }
     }
-    if constexpr (p4 & 1) wait_vmem();
-    barrier_lds();
+    // Odd slots end the tile: the loads issued in the even slot have landed
+    // (each wave waits for its own) and every wave is done with the buffers
+    // that the next even slot refills.  The even slots need no barrier.
+    if constexpr (p4 & 1) {
+      wait_vmem();
+      barrier_lds();
+    }
   };
 
   wait_vmem();
@@ -287,7 +296,7 @@ void fwd_kernel(FwdParams p) {
   else run(Int<1>{});
 
   // ---- epilogue: O = Oᵀ / l, LSE = m + log2(l) in natural log.
-  const float lt = l + xor32(l);
+  const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
 #pragma unroll
