@@ -16,6 +16,17 @@ oracle).
 
 Prints one JSON line.  `--gpus` above 1 is refused: this build runs on a
 single GPU.
+
+Two helper modes produce the measured HBM traffic that the roofline objects
+report (see `profiles/`):
+  python bench.py --profile-once
+      runs every kernel of the step and the decode once, plus a 1 GiB device
+      copy whose byte count calibrates the counters; run it under
+      `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE`;
+  python bench.py --traffic-from FETCH.csv WRITE.csv
+      turns the two counter CSVs into profiles/traffic.json (bytes per launch,
+      scaled by the copy's known bytes, tagged with the kernels' source hash)
+      and profiles/hbm_traffic_mha_bf16_4k_and_decode.md.
 """
 
 from __future__ import annotations
@@ -206,6 +217,105 @@ def cpu_baseline(si, budget_s: float):
                       f"float64 numpy, {el:.1f} s; flops counted as for the GPU (visible pairs only)"}
 
 
+def profile_once(torch, fa, si):
+    """One launch of every kernel of the training step and of the decode, then
+    a 1 GiB device-to-device copy (counter calibration)."""
+    w = si.WORKLOADS["mha_bf16_4k"]
+    q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, fa.FA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, True)
+    fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, True)
+    fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, True)
+    torch.cuda.synchronize()
+    del q, k, v, do, o, lse, ws, dq, dk, dv
+    wd = si.WORKLOADS["decode_gqa_paged"]
+    args = [t.to("cuda") for t in si.workload_decode_inputs(wd)]
+    fa.decode_paged(*args)
+    torch.cuda.synchronize()
+    del args
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print("profile-once done", flush=True)
+
+
+COPY_BYTES = 1 << 30
+# rocprofv3 kernel names -> the keys used above (the decode is split + reduce).
+KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_kernel", "dkdv"),
+               ("bwd_dq_kernel", "dq"), ("decode_split_kernel", "decode"), ("decode_reduce_kernel", "decode"))
+
+
+def _counter_sums(path, counter):
+    """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, val = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, val + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_csv, write_csv):
+    fetch, write = _counter_sums(fetch_csv, "FETCH_SIZE"), _counter_sums(write_csv, "WRITE_SIZE")
+    def per_key(rows):
+        acc, copy = {}, []
+        for name, kib in rows.values():
+            if "copy" in name.lower() or "elementwise" in name.lower():
+                copy.append(kib)
+                continue
+            for pat, key in KERNEL_KEYS:
+                if pat in name:
+                    acc.setdefault(key, {}).setdefault(pat, []).append(kib)
+        # bytes per launch: mean over dispatches of each kernel, summed over the key's kernels
+        return {k: sum(sum(v) / len(v) for v in pats.values()) * 1024 for k, pats in acc.items()}, copy
+    fb, fcopy = per_key(fetch)
+    wb, wcopy = per_key(write)
+    if not fcopy or not wcopy:
+        raise SystemExit("no calibration copy kernel found in the counter files")
+    f_factor = COPY_BYTES / (max(fcopy) * 1024)
+    w_factor = COPY_BYTES / (max(wcopy) * 1024)
+    rec = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": round(f_factor, 4),
+                            "write_factor": round(w_factor, 4),
+                            "note": "counter KiB x 1024 x factor = bytes; factor = copy bytes / copy counter bytes"}}
+    for key in sorted(set(fb) | set(wb)):
+        fbytes, wbytes = fb.get(key, 0.0) * f_factor, wb.get(key, 0.0) * w_factor
+        rec[key] = {"fetch_bytes": round(fbytes), "write_bytes": round(wbytes),
+                    "hbm_bytes_per_launch": round(fbytes + wbytes),
+                    "source_hash": source_hash(*KERNEL_SOURCES[key])}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    # Text summary next to it.
+    w = None
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Workloads: mha_bf16_4k (B=2, H=16, N=4096, d=128, causal, bf16) for fwd / prep / dkdv / dq;",
+             "decode_gqa_paged (B=8, Hq=32, Hkv=8, Nk=32768, d=128, bf16, 16-token pages) for decode.", "",
+             "Commands (from the repository root, on the GPU):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- python3 bench.py --profile-once",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- python3 bench.py --profile-once",
+             "    python3 bench.py --traffic-from gpurun_out/pmc_fetch/p_counter_collection.csv gpurun_out/pmc_write/p_counter_collection.csv",
+             "",
+             f"Calibration: a {COPY_BYTES >> 20} MiB device copy reads and writes {COPY_BYTES} bytes; the counters report "
+             f"{max(fcopy):.0f} KiB fetched and {max(wcopy):.0f} KiB written, so fetch counts scale by {f_factor:.4f} "
+             f"and write counts by {w_factor:.4f}.", "",
+             "| kernel | fetch bytes | write bytes | total per launch |", "|---|---:|---:|---:|"]
+    for key in ("fwd", "prep", "dkdv", "dq", "decode"):
+        if key in rec:
+            r = rec[key]
+            lines.append(f"| {key} | {r['fetch_bytes']:,} | {r['write_bytes']:,} | {r['hbm_bytes_per_launch']:,} |")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_mha_bf16_4k_and_decode.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,7 +324,13 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-once", action="store_true", help="launch every kernel once (for rocprofv3 counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention kernels here are "
               "built and timed on a single MI355X and no multi-GPU path exists.", file=sys.stderr)
@@ -228,6 +344,9 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     props = torch.cuda.get_device_properties(0)
+    if args.profile_once:
+        profile_once(torch, fa, si)
+        return 0
 
     w, ms_step, per, wall = bench_training(torch, fa, si, args.steps, args.warmup)
     fl = attention_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True)
