@@ -232,39 +232,63 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
   }
 }
 
-// One wave per (sequence, query head).  Lanes first reduce the splits' maxima
-// and sums in parallel (64 splits per round, fixed order, so the result is
-// deterministic), then each lane accumulates its d values over the splits.
-template <typename T, int D>
+// One wave per (sequence, query head), two memory round trips: lane s loads
+// split s's max and sum (64 splits per round) while every lane loads its d
+// values of all splits, then the wave reduces.  Splits are merged in a fixed
+// order, so the result is deterministic.
+template <typename T, int D, int SMAX>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const float* __restrict__ part, T* __restrict__ out,
                                                            float* __restrict__ lse, int splits) {
   constexpr int kRec = D + 4;
+  constexpr int kPer = (D + 63) / 64;
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* rec = part + (size_t)bh * splits * kRec;
-  float M = -INFINITY;
-  for (int s = lane; s < splits; s += 64) M = fmaxf(M, rec[(size_t)s * kRec + D]);
+  // Round trip 1 (issued together with round trip 2 below): split maxima and sums.
+  float ms_l = -INFINITY, ls_l = 0.f;
+  if (lane < splits) { ms_l = rec[(size_t)lane * kRec + D]; ls_l = rec[(size_t)lane * kRec + D + 1]; }
+  float v[SMAX][kPer];
+  if (splits <= SMAX) {
+#pragma unroll
+    for (int s = 0; s < SMAX; s++)
+#pragma unroll
+      for (int j = 0; j < kPer; j++) {
+        const int d = lane + 64 * j;
+        v[s][j] = (s < splits && d < D) ? rec[(size_t)s * kRec + d] : 0.f;
+      }
+  }
+  float M = ms_l;
+  for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, rec[(size_t)s * kRec + D]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float L = 0.f;
-  for (int s = lane; s < splits; s += 64) {
+  float L = ms_l == -INFINITY ? 0.f : ls_l * fast_exp2(ms_l - M);
+  for (int s = lane + 64; s < splits; s += 64) {
     const float ms = rec[(size_t)s * kRec + D];
     if (ms != -INFINITY) L = fmaf(rec[(size_t)s * kRec + D + 1], fast_exp2(ms - M), L);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-  constexpr int kPer = (D + 63) / 64;
+  // Weight of split s: 2^(m_s - M), 0 for splits that saw no key.
+  const float wl = ms_l == -INFINITY ? 0.f : fast_exp2(ms_l - M);
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; j++) acc[j] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < splits; s++) {
-    const float* r = rec + (size_t)s * kRec;
-    const float ms = r[D];
-    const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+  if (splits <= SMAX) {
 #pragma unroll
-    for (int j = 0; j < kPer; j++) {
-      const int d = lane + 64 * j;
-      if (d < D) acc[j] = fmaf(r[d], wgt, acc[j]);
+    for (int s = 0; s < SMAX; s++) {
+      const float wgt = __shfl(wl, s, 64);
+#pragma unroll
+      for (int j = 0; j < kPer; j++) acc[j] = fmaf(v[s][j], wgt, acc[j]);
+    }
+  } else {
+    for (int s = 0; s < splits; s++) {
+      const float* r = rec + (size_t)s * kRec;
+      const float ms = r[D];
+      const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+#pragma unroll
+      for (int j = 0; j < kPer; j++) {
+        const int d = lane + 64 * j;
+        if (d < D) acc[j] = fmaf(r[d], wgt, acc[j]);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -291,8 +315,13 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
                      a.seq_lens, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream, a.part, (T*)a.o, a.lse,
-                     a.splits);
+  // Up to 32 splits are merged from registers loaded in one round trip.
+  if (a.splits <= 16)
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, 16>), dim3(a.B * a.Hq), dim3(64), 0, stream, a.part, (T*)a.o,
+                       a.lse, a.splits);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, 32>), dim3(a.B * a.Hq), dim3(64), 0, stream, a.part, (T*)a.o,
+                       a.lse, a.splits);
   return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ CASES = [
     (1, 16, 1, [777], 64, "bf16", 1),
     (2, 24, 2, [250, 1], 128, "bf16", 64),      # more splits than pages
     (1, 8, 8, [4096], 128, "f16", 0),
+    (2, 8, 2, [1500, 2000], 128, "bf16", 16),   # reduce: splits fill the 16-register merge
+    (1, 12, 4, [3000], 64, "f16", 27),          # reduce: 32-register merge, partly used
+    (1, 4, 4, [5000], 32, "bf16", 33),          # reduce: past the register merge (loop path)
 ]
 
 
