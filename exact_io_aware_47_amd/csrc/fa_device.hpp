@@ -68,6 +68,9 @@ template <> struct Elem<__bf16> {
     return f;
   }
   __device__ static __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+  __device__ static __forceinline__ Frag negate(const Frag& f) {  // flip the sign bits (exact)
+    return __builtin_bit_cast(Frag, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
+  }
 };
 
 template <> struct Elem<_Float16> {
@@ -83,6 +86,9 @@ template <> struct Elem<_Float16> {
     return f;
   }
   __device__ static __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+  __device__ static __forceinline__ Frag negate(const Frag& f) {
+    return __builtin_bit_cast(Frag, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
+  }
 };
 
 struct F32Frag { float v[8]; };
@@ -102,6 +108,11 @@ template <> struct Elem<float> {
     return f;
   }
   __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ Frag negate(Frag f) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) f.v[i] = -f.v[i];
+    return f;
+  }
 };
 
 // --------------------------------------------------------------------------

@@ -122,6 +122,10 @@ void fwd_kernel(FwdParams p) {
   Frag qf[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ks++) qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
+  if (p.c < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ks++) qf[ks] = E::negate(qf[ks]);
+  }
 
   // Per-lane LDS offsets of the K row fragments (A rows are sigma-permuted
   // keys) and of the V column fragments; M tiles / k blocks add constants.
@@ -142,7 +146,10 @@ void fwd_kernel(FwdParams p) {
   Frag pf[C::kPS];      // probabilities of the last softmax, consumed by the next PV
   float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
   float l = 0.f;        // this lane's share of the running sum (the other half-wave holds the rest)
-  const bool fast_ok = p.c > 0.f;
+  // The max of c*s over a row is c*max(s) only for c > 0: a negative scale
+  // flips the sign of Q instead (exact), a zero scale becomes a tiny positive
+  // one (every exp2 then rounds to 1, as exp2(0) would).
+  const float c = p.c < 0.f ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
 
   // Does this wave see any key of tile j?
   auto active = [&](int j) __attribute__((always_inline)) { return j < n_tiles && (!CAUSAL || j * C::kBC <= qw + 31 + diag); };
@@ -175,37 +182,40 @@ void fwd_kernel(FwdParams p) {
       }
     }
     if constexpr (k16) sched_reads_ahead<2 * C::kPS * C::kDT, C::kPS * C::kDT, 4>();
+    // Row sums of this P in float32, still in s until S of the next tile
+    // overwrites it; added here because the softmax phase is the busier one.
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
   // Register r of M tile mt holds key k0 + 32*mt + 16*(r/8) + 8h + (r%8).
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * C::kBC;
-    const bool need_mask = !fast_ok || (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
-    float mx;
-    if (!need_mask) {
-      // Four independent three-input max chains.
-      float x[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-        for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
-#pragma unroll
-          for (int i = 0; i < 4; i++)
-            x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
-      mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * p.c;
-    } else {
-      mx = -INFINITY;
+    // Invisible keys (past Nk, past the causal horizon) get score -inf; the
+    // rest of the softmax is one code path for every tile.
+    if ((k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
       const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
 #pragma unroll
       for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int key = k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7);
-          const float t = key <= horizon ? s[mt][r] * p.c : -INFINITY;
-          s[mt][r] = t;
-          mx = fmaxf(mx, t);
+          if (key > horizon) s[mt][r] = -INFINITY;
         }
-      mx = max_halves(mx);
     }
+    // Four independent three-input max chains; c > 0, so max(c s) = c max(s).
+    float x[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
+    const float mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * c;
     // Move the running max only if it grows by more than kTau.
     const bool grow = mx > m + kTau;
     if (__any(grow)) {
@@ -217,23 +227,11 @@ void fwd_kernel(FwdParams p) {
       for (int dt = 0; dt < C::kDT; dt++) o[dt] *= alpha;
     }
     const float m_use = m == -INFINITY ? 0.f : m;  // rows that have seen no key yet
-    if (!need_mask) {
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(fmaf(s[mt][r], p.c, -m_use));
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; mt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(s[mt][r] - m_use);
-    }
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
-    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      for (int r = 0; r < 16; r++) s[mt][r] = fast_exp2(fmaf(s[mt][r], c, -m_use));
+    // (The row sums of P are added in the next PV phase.)
     // Pᵀ k block ps = registers 8*(ps%2).. of tile ps/2.
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
@@ -267,7 +265,14 @@ void fwd_kernel(FwdParams p) {
         const int j = u >> 1;
         constexpr int jp = ((p4 - g + 4) >> 1) & 1;  // parity of j
         if (j >= 1 && active(j - 1)) gemm_pv(vbuf(jp ^ 1));
+        // s is (re)defined on both paths, so the probabilities left in it by
+        // the last softmax are dead after PV: a tile that skips S also skips
+        // its softmax, so any value will do.
         if (active(j)) gemm_s(kbuf(jp));
+        else {
+#pragma unroll
+          for (int mt = 0; mt < C::kMT; mt++) s[mt] = __builtin_nondeterministic_value(s[mt]);
+        }
       } else {
         const int j = (u - 1) >> 1;
         if (active(j)) softmax(j);
