@@ -36,6 +36,23 @@
 namespace fa {
 namespace {
 
+// Schedule of the interleaved PV/S sequence: each step is one PV product
+// (two transposing reads) and one S product (one row read); the reads of the
+// first PD steps go up front, then every step's products are followed by the
+// reads of the step PD places later.
+template <int N, int PD>
+__device__ __forceinline__ void sched_pv_s() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  constexpr int pd = PD < N ? PD : N;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 3 * pd, 0);
+#pragma unroll
+  for (int i = 0; i < N - pd; i++) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 3, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, 2 * pd, 0);
+}
+
 template <typename T, int D>
 struct FwdCfg {
   static constexpr int kWaves = 8;
@@ -144,6 +161,21 @@ void fwd_kernel(FwdParams p) {
   for (int dt = 0; dt < C::kDT; dt++) o[dt] = f32x16{};
   f32x16 s[C::kMT];     // scores of the last S, consumed by the next softmax
   Frag pf[C::kPS];      // probabilities of the last softmax, consumed by the next PV
+  // 16-bit types run PV of tile j-1 and S of tile j as one sequence from tile
+  // 0 on: the first one multiplies zero probabilities by a zeroed V buffer and
+  // sums zero scores, so it adds nothing.
+#pragma unroll
+  for (int mt = 0; mt < C::kMT; mt++) s[mt] = f32x16{};
+#pragma unroll
+  for (int ps = 0; ps < C::kPS; ps++) pf[ps] = Frag{};
+  if constexpr (k16) {
+    // Zero the second K and V buffers (V(-1) of that first sequence, and the
+    // K read past the last tile, whose scores are never used).
+    for (int i = threadIdx.x; i < C::kTileBytes / 16; i += 64 * C::kWaves) {
+      *(__attribute__((address_space(3))) u32x4*)(kbuf(1) + 16 * i) = u32x4{0, 0, 0, 0};
+      *(__attribute__((address_space(3))) u32x4*)(vbuf(1) + 16 * i) = u32x4{0, 0, 0, 0};
+    }
+  }
   float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
   float l = 0.f;        // this lane's share of the running sum (the other half-wave holds the rest)
   // The max of c*s over a row is c*max(s) only for c > 0: a negative scale
@@ -190,6 +222,35 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+  // PV of the last tile and S of this tile in one interleaved sequence (16-bit
+  // types): step i issues one PV and one S product (both counts equal
+  // kBC*D/512), so the slower transposing V reads and the K row reads share
+  // the LDS evenly instead of arriving in two bursts.  The row sums of the
+  // last P are taken from s first, so the new S can take its registers.
+  auto gemm_fused = [&](const lds_char* vb, const lds_char* kb) __attribute__((always_inline)) {
+    if constexpr (k16) {
+    constexpr int N = C::kPS * C::kDT;
+    static_assert(N == C::kKS * C::kMT, "PV and S have equal product counts");
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++) s[mt] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int ps = i / C::kDT, dt = i % C::kDT;
+      const Frag av = F::lds_col_at(vb + 16 * ps * C::kRowBytes, voff[dt][0], voff[dt][1]);
+      o[dt] = E::mma(av, pf[ps], o[dt]);
+      const int ks = i / C::kMT, mt = i % C::kMT;
+      const Frag ak = F::lds_row_at(kb + 32 * mt * C::kRowBytes, koff[ks]);
+      s[mt] = E::mma(ak, qf[ks], s[mt]);
+    }
+    sched_pv_s<N, 3>();
+    }
   };
   // Register r of M tile mt holds key k0 + 32*mt + 16*(r/8) + 8h + (r%8).
   auto softmax = [&](int j) __attribute__((always_inline)) {
@@ -264,14 +325,20 @@ void fwd_kernel(FwdParams p) {
       if constexpr (((p4 - g) & 1) == 0) {
         const int j = u >> 1;
         constexpr int jp = ((p4 - g + 4) >> 1) & 1;  // parity of j
-        if (j >= 1 && active(j - 1)) gemm_pv(vbuf(jp ^ 1));
-        // s is (re)defined on both paths, so the probabilities left in it by
-        // the last softmax are dead after PV: a tile that skips S also skips
-        // its softmax, so any value will do.
-        if (active(j)) gemm_s(kbuf(jp));
-        else {
+        // active() is monotone in j for a wave (tile j active implies tile j-1
+        // active), so this runs PV(j-1) whenever it is due and S(j) with it.
+        if (k16) {
+          if (j == 0 ? active(0) : active(j - 1)) gemm_fused(vbuf(jp ^ 1), kbuf(jp));
+        } else {
+          if (j >= 1 && active(j - 1)) gemm_pv(vbuf(jp ^ 1));
+          // s is (re)defined on both paths, so the probabilities left in it by
+          // the last softmax are dead after PV: a tile that skips S also skips
+          // its softmax, so any value will do.
+          if (active(j)) gemm_s(kbuf(jp));
+          else {
 #pragma unroll
-          for (int mt = 0; mt < C::kMT; mt++) s[mt] = __builtin_nondeterministic_value(s[mt]);
+            for (int mt = 0; mt < C::kMT; mt++) s[mt] = __builtin_nondeterministic_value(s[mt]);
+          }
         }
       } else {
         const int j = (u - 1) >> 1;
