@@ -216,23 +216,29 @@ void bwd_dkdv_kernel(DkvParams p) {
     if constexpr (C::kES == 2) sched_reads_ahead<2 * C::kKS * C::kMT, 2 * C::kKS * C::kMT, 4>();
     // ---- P and dS.  Register r of M tile mt holds query
     //      i0 + 32*mt + 16*(r/8) + 8h + (r%8) for this lane's key.
-    const bool need_mask = CAUSAL && kw + 31 > i0 + diag;
+    //      Only steps that cross the causal diagonal mask P (a uniform branch).
+    float dd[C::kMT][2][8];
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        float l2[8], dd[8];
+        float l2[8];
         lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
-        lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
+        lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd[mt][u]);
 #pragma unroll
-        for (int t = 0; t < 8; t++) {
-          const int r = 8 * u + t;
-          float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2[t]));
-          if (need_mask && key > i0 + 32 * mt + 16 * u + 8 * h + t + diag) pr = 0.f;
-          sv[mt][r] = pr;
-          dp[mt][r] = pr * (dp[mt][r] - dd[t]);
-        }
+        for (int t = 0; t < 8; t++) sv[mt][8 * u + t] = fast_exp2(fmaf(sv[mt][8 * u + t], p.c, -l2[t]));
       }
+    if (CAUSAL && kw + 31 > i0 + diag) {
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (key > i0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) + diag) sv[mt][r] = 0.f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] - dd[mt][r >> 3][r & 7]);
     // ---- dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (column = key, k = query).
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
