@@ -433,16 +433,23 @@ void bwd_dq_kernel(DqParams p) {
     // ---- dSᵀ = Pᵀ ∘ (dPᵀ - D).  Register r of tile mt holds key
     //      k0 + 32*mt + 16*(r/8) + 8h + (r%8).  Keys past Nk are masked too
     //      (their zero-filled rows must not meet an infinite P).
-    const bool need_mask = (k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag);
-    const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float pr = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
-        if (need_mask && k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) > horizon) pr = 0.f;
-        dp[mt][r] = pr * (dp[mt][r] - dd);
-      }
+      for (int r = 0; r < 16; r++) sv[mt][r] = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
+    // Only tiles cut by Nk or by the causal diagonal mask P (a uniform branch).
+    if ((k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
+      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) > horizon) sv[mt][r] = 0.f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::kMT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] - dd);
     // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
