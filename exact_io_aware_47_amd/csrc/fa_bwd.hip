@@ -299,6 +299,259 @@ void bwd_dkdv_kernel(DkvParams p) {
     }
 }
 
+// Schedule of phase A of the pipelined dK/dV step: the NS row-statistics
+// reads go first, then the transposing reads of the first PD products, then
+// each product is followed by up to NV VALU instructions and the reads of the
+// product PD places later.
+template <int NS, int NR, int NM, int NV, int PD, int I = 0>
+__device__ __forceinline__ void sched_phase_a() {
+  constexpr int kMfma = 0x008, kValu = 0x002 | 0x400, kDsRead = 0x100;
+  constexpr int r = NR / NM;
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, NS + PD * r, 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, NV, 0);
+    if constexpr (I + PD < NM) __builtin_amdgcn_sched_group_barrier(kDsRead, r, 0);
+    sched_phase_a<NS, NR, NM, NV, PD, I + 1>();
+  }
+}
+
+// dK, dV for 16-bit types, software-pipelined.  One wave per SIMD owns 32
+// keys (as above); across the query steps of the work-group the matrix core
+// and the VALU overlap:
+//   phase A of step i:  P(i), dS(i) on the VALU   |  dVᵀ, dKᵀ += ... of step i-1
+//   phase B of step i:  S, dP of step i+1 on the matrix core
+// Steps live in four LDS buffers (step i+2 is loaded at the top of step i
+// into the buffer of step i-2); phase B waits for step i+1's loads and a
+// barrier.  Masked scores are set to -inf before the exponential; a negative
+// scale flips the sign of K instead, a zero scale becomes a tiny positive
+// one, so P is 0 there with no NaN.  The first phase A multiplies zero
+// probabilities by a zeroed buffer, so it adds nothing.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv16_kernel(DkvParams p) {
+  using C = DkvCfg<T, D>;
+  using E = Elem<T>;
+  using F = Frags<T>;
+  using TT = Tile<C::kRowBytes>;
+  typedef typename E::Frag Frag;
+  constexpr int KS = C::kKS, MT = C::kMT, PS = C::kPS, DT = C::kDT;
+
+  __shared__ __attribute__((aligned(1024))) char q_l0[C::kTileBytes], q_l1[C::kTileBytes], q_l2[C::kTileBytes],
+      q_l3[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char do_l0[C::kTileBytes], do_l1[C::kTileBytes], do_l2[C::kTileBytes],
+      do_l3[C::kTileBytes];
+  __shared__ __attribute__((aligned(512))) char st_l0[C::kStatBytes], st_l1[C::kStatBytes], st_l2[C::kStatBytes],
+      st_l3[C::kStatBytes];
+  auto qbuf = [&](int i) __attribute__((always_inline)) {
+    return (lds_char*)(i == 0 ? q_l0 : i == 1 ? q_l1 : i == 2 ? q_l2 : q_l3);
+  };
+  auto dobuf = [&](int i) __attribute__((always_inline)) {
+    return (lds_char*)(i == 0 ? do_l0 : i == 1 ? do_l1 : i == 2 ? do_l2 : do_l3);
+  };
+  auto stbuf = [&](int i) __attribute__((always_inline)) {
+    return (lds_char*)(i == 0 ? st_l0 : i == 1 ? st_l1 : i == 2 ? st_l2 : st_l3);
+  };
+
+  const int bh_count = p.B * p.Hkv;
+  const int id = blockIdx.x;
+  const int bhk = id % bh_count;
+  const int kt = id / bh_count;
+  const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
+  const int g = p.Hq / p.Hkv;
+
+  const int lane = lane_id(), w = wave_id();
+  const int h = lane >> 5, col = lane & 31;
+  const int k0 = kt * C::kBKV;
+  const int kw = k0 + 32 * w;
+  const int key = kw + col;
+  const int diag = p.Nk - p.Nq;
+  const bool neg = p.c < 0.f;
+  const float c = neg ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+
+  const size_t kv_slab = (size_t)bhk * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+
+  const int n_qt = (p.Nq + C::kBQ - 1) / C::kBQ;
+  const int qt0 = CAUSAL ? max(0, k0 - diag) / C::kBQ : 0;
+  const int per_head = n_qt - qt0;
+  const int steps = g * per_head;
+
+  // Loads of step s into buffer buf.  A step past the end (valid false)
+  // issues the same instructions on empty ranges, which read nothing, so
+  // every step issues the same number of loads and needs no branch.
+  auto load_step = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
+    s = valid ? s : 0;
+    const int hq = hkv * g + s / per_head;
+    const int qt = qt0 + s % per_head;
+    const size_t bhq = (size_t)b * p.Hq + hq;
+    const size_t q_slab = bhq * p.Nq * D;
+    const uint32_t bytes = valid ? (uint32_t)p.Nq * C::kRowBytes : 0u;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * 2, bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * 2, bytes);
+    const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, qbuf(buf), w, lane);
+    dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, dobuf(buf), w, lane);
+    // The step's row statistics: wave 0 stages lse2 and wave 1 dsum, one
+    // 16-lane load each, so every wave's count of loads per step is exact.
+    if (w < 2 && lane < 16) {
+      const float* src = (w == 0 ? p.lse2 : p.dsum) + bhq * p.Nq;
+      buf_load16_to_lds(make_rsrc(src, valid ? (uint32_t)p.Nq * 4 : 0u), (uint32_t)qt * C::kBQ * 4 + lane * 16,
+                        stbuf(buf) + w * 256);
+    }
+  };
+  auto first_row = [&](int s) __attribute__((always_inline)) { return (qt0 + s % per_head) * C::kBQ; };
+
+  if (steps > 0) load_step(0, 0, true);
+  if (steps > 1) load_step(1, 1, true);
+
+  // Kᵀ and Vᵀ as B operands (k = d, column = this lane's key).
+  Frag kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    kf[ks] = F::template global_row<D>(rk, key, ks, h);
+    vf[ks] = F::template global_row<D>(rv, key, ks, h);
+    if (neg) kf[ks] = E::negate(kf[ks]);
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
+  uint32_t roff[KS], coff[DT][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) roff[ks] = F::template row_off<TT>(sigma(col), ks, h);
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+    for (int u = 0; u < 2; u++) coff[dt][u] = F::template col_off<TT>(32 * dt, u, lane);
+
+  // Buffer 3 stands for step -1 of the first phase A: zero it.
+  for (int i = threadIdx.x; i < C::kTileBytes / 16; i += 256) {
+    *(__attribute__((address_space(3))) u32x4*)(qbuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
+    *(__attribute__((address_space(3))) u32x4*)(dobuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 sv[MT], dp[MT];
+  Frag pa[PS], da[PS], pb[PS], db[PS];  // P and dS fragments of two consecutive steps
+#pragma unroll
+  for (int ps = 0; ps < PS; ps++) { pa[ps] = Frag{}; da[ps] = Frag{}; pb[ps] = Frag{}; db[ps] = Frag{}; }
+
+  // S = Q Kᵀ and dP = dO Vᵀ of one step (A rows: sigma-permuted queries).
+  auto gemm_sdp = [&](const lds_char* qb, const lds_char* dob) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        sv[mt] = E::mma(F::lds_row_at(qb + 32 * mt * C::kRowBytes, roff[ks]), kf[ks], sv[mt]);
+        dp[mt] = E::mma(F::lds_row_at(dob + 32 * mt * C::kRowBytes, roff[ks]), vf[ks], dp[mt]);
+      }
+  };
+  // Register r of M tile mt holds query i0 + 32*mt + 16*(r/8) + 8h + (r%8).
+  auto mask = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (key > i0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7) + diag) sv[mt][r] = -INFINITY;
+  };
+  // P = exp2(c s - lse2), dS = P (dP - D), both rounded to T as B operands.
+  auto p_ds = [&](const lds_char* stb, Frag (&pn)[PS], Frag (&dn)[PS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        float l2[8], dd[8], pv[8], dsv[8];
+        lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
+        lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          pv[t] = fast_exp2(fmaf(sv[mt][8 * u + t], c, -l2[t]));
+          dsv[t] = pv[t] * (dp[mt][8 * u + t] - dd[t]);
+        }
+        pn[2 * mt + u] = E::pack(pv);
+        dn[2 * mt + u] = E::pack(dsv);
+      }
+  };
+  // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS of one step (column = key, k = query).
+  auto gemm_dvdk = [&](const lds_char* qb, const lds_char* dob, const Frag (&pf)[PS], const Frag (&dsf)[PS])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int ps = 0; ps < PS; ps++)
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        dv[dt] = E::mma(F::lds_col_at(dob + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]), pf[ps], dv[dt]);
+        dk[dt] = E::mma(F::lds_col_at(qb + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]), dsf[ps], dk[dt]);
+      }
+  };
+
+  constexpr int kDmaPerStep =
+      2 * ((C::kBQ * C::kRowBytes / 1024) >= C::kWaves ? (C::kBQ * C::kRowBytes / 1024) / C::kWaves : 1);
+
+  // Step i (bi = i mod 4; P/dS of step i go to (pn, dn), those of step i-1 are (po, dob_)).
+  auto iter = [&](auto bc, Frag (&pn)[PS], Frag (&dn)[PS], const Frag (&po)[PS], const Frag (&dq_)[PS], int i)
+      __attribute__((always_inline)) {
+    constexpr int bi = decltype(bc)::value;
+    load_step(i + 2, (bi + 2) & 3, i + 2 < steps);
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+      asm volatile("" : "+a"(dk[dt]));
+      asm volatile("" : "+a"(dv[dt]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      asm volatile("" : "+a"(kf[ks]));
+      asm volatile("" : "+a"(vf[ks]));
+    }
+    // Past the last step sv/dp hold stale values; their P/dS are never used.
+    if (CAUSAL && i < steps && kw + 31 > first_row(i) + diag) mask(first_row(i));
+    // Phase A.
+    p_ds(stbuf(bi), pn, dn);
+    gemm_dvdk(qbuf((bi + 3) & 3), dobuf((bi + 3) & 3), po, dq_);
+    sched_phase_a<4 * MT, 4 * PS * DT, 2 * PS * DT, 5, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    // Step i+1's loads (issued one step ago) must have landed; this step's
+    // loads (kDmaPerStep per wave, plus one stats load on waves 0 and 1) may
+    // stay in flight: loads retire in issue order.
+    if (w < 2) wait_vmem_le<kDmaPerStep + 1>();
+    else wait_vmem_le<kDmaPerStep>();
+    barrier_lds();
+    // Phase B.
+    if (i + 1 < steps) {
+      gemm_sdp(qbuf((bi + 1) & 3), dobuf((bi + 1) & 3));
+      sched_mfma_valu_reads<2 * KS * MT, 2 * KS * MT, 0, 4>();
+    }
+  };
+
+  wait_vmem();
+  barrier_lds();
+  if (steps > 0) gemm_sdp(qbuf(0), dobuf(0));
+  // steps + 1 iterations: the last one only completes dV/dK of the last step.
+  int i = 0;
+  for (; i + 4 <= steps + 1; i += 4) {
+    iter(Int<0>{}, pb, db, pa, da, i);
+    iter(Int<1>{}, pa, da, pb, db, i + 1);
+    iter(Int<2>{}, pb, db, pa, da, i + 2);
+    iter(Int<3>{}, pa, da, pb, db, i + 3);
+  }
+  if (i <= steps) iter(Int<0>{}, pb, db, pa, da, i);
+  if (i + 1 <= steps) iter(Int<1>{}, pa, da, pb, db, i + 1);
+  if (i + 2 <= steps) iter(Int<2>{}, pb, db, pa, da, i + 2);
+
+  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const uint32_t off = (uint32_t)key * C::kRowBytes + (32 * dt + 8 * a4 + 4 * h) * 2;
+      F::store4(wk, off, dk[dt][4 * a4] * p.scale, dk[dt][4 * a4 + 1] * p.scale, dk[dt][4 * a4 + 2] * p.scale,
+                dk[dt][4 * a4 + 3] * p.scale);
+      F::store4(wv, off, dv[dt][4 * a4], dv[dt][4 * a4 + 1], dv[dt][4 * a4 + 2], dv[dt][4 * a4 + 3]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dQ (Q-outer)
 // ---------------------------------------------------------------------------
@@ -529,7 +782,13 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
   p.c = a.scale * kLog2e; p.scale = a.scale;
   const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  // The pipelined kernel wins when every work-group walks all query tiles;
+  // under the causal mask most work-groups are short and the plain kernel,
+  // which has no pipeline to fill and drain, is faster.
+  if constexpr (Elem<T>::kBytes == 2 && !CAUSAL)
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

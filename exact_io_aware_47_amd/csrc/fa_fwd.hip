@@ -80,7 +80,6 @@ struct FwdParams {
 
 constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
 
-template <int N> struct Int { static constexpr int value = N; };
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
