@@ -299,34 +299,21 @@ void bwd_dkdv_kernel(DkvParams p) {
     }
 }
 
-// Schedule of phase A of the pipelined dK/dV step: the NS row-statistics
-// reads go first, then the transposing reads of the first PD products, then
-// each product is followed by up to NV VALU instructions and the reads of the
-// product PD places later.
-template <int NS, int NR, int NM, int NV, int PD, int I = 0>
-__device__ __forceinline__ void sched_phase_a() {
-  constexpr int kMfma = 0x008, kValu = 0x002 | 0x400, kDsRead = 0x100;
-  constexpr int r = NR / NM;
-  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, NS + PD * r, 0);
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kValu, NV, 0);
-    if constexpr (I + PD < NM) __builtin_amdgcn_sched_group_barrier(kDsRead, r, 0);
-    sched_phase_a<NS, NR, NM, NV, PD, I + 1>();
-  }
-}
-
 // dK, dV for 16-bit types, software-pipelined.  One wave per SIMD owns 32
-// keys (as above); across the query steps of the work-group the matrix core
-// and the VALU overlap:
-//   phase A of step i:  P(i), dS(i) on the VALU   |  dVᵀ, dKᵀ += ... of step i-1
-//   phase B of step i:  S, dP of step i+1 on the matrix core
-// Steps live in four LDS buffers (step i+2 is loaded at the top of step i
-// into the buffer of step i-2); phase B waits for step i+1's loads and a
-// barrier.  Masked scores are set to -inf before the exponential; a negative
-// scale flips the sign of K instead, a zero scale becomes a tiny positive
-// one, so P is 0 there with no NaN.  The first phase A multiplies zero
-// probabilities by a zeroed buffer, so it adds nothing.
+// keys (as above).  Step i of the main loop overlaps, within each wave,
+//   P(i), dS(i) on the VALU   with   dVᵀ, dKᵀ += ... of step i-1  and
+//                                    S, dP of step i+1 on the matrix core.
+// The products run in chunks of four, fenced from each other, and the P/dS
+// work is cut into stages that follow a fixed chunk schedule (see fused).
+// Steps rotate through four LDS buffers: step i+2 is loaded at the top of
+// step i into the buffer of step i-2, after a barrier that both publishes
+// step i+1's tiles and frees that buffer.
+// Under the causal mask the query tiles that cross the diagonal (at most the
+// first three of each head) are done first, one at a time with a masked step;
+// the pipelined steps then mask nothing.  Masked scores are set to -inf
+// before the exponential; a negative scale flips the sign of K instead, a
+// zero scale becomes a tiny positive one, so P is 0 there with no NaN.  The
+// first pipelined step multiplies P/dS by a zeroed buffer, so it adds nothing.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv16_kernel(DkvParams p) {
@@ -341,8 +328,12 @@ void bwd_dkdv16_kernel(DkvParams p) {
       q_l3[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char do_l0[C::kTileBytes], do_l1[C::kTileBytes], do_l2[C::kTileBytes],
       do_l3[C::kTileBytes];
-  __shared__ __attribute__((aligned(512))) char st_l0[C::kStatBytes], st_l1[C::kStatBytes], st_l2[C::kStatBytes],
-      st_l3[C::kStatBytes];
+  // Row statistics of a step: lse2 in the first 256 bytes, dsum in the next;
+  // every wave owns one 256-byte slot that its stats load writes.
+  constexpr int kStatArea = 256 * C::kWaves;
+  static_assert(C::kBQ * 4 == 256, "a step's rows fill one slot");
+  __shared__ __attribute__((aligned(1024))) char st_l0[kStatArea], st_l1[kStatArea], st_l2[kStatArea],
+      st_l3[kStatArea];
   auto qbuf = [&](int i) __attribute__((always_inline)) {
     return (lds_char*)(i == 0 ? q_l0 : i == 1 ? q_l1 : i == 2 ? q_l2 : q_l3);
   };
@@ -373,19 +364,22 @@ void bwd_dkdv16_kernel(DkvParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
 
+  // Query tiles per head that see this work-group's keys: the first n_diag
+  // of them cross the causal diagonal (every later row sees all 128 keys),
+  // the other n_rest form the pipelined steps, head after head.
   const int n_qt = (p.Nq + C::kBQ - 1) / C::kBQ;
   const int qt0 = CAUSAL ? max(0, k0 - diag) / C::kBQ : 0;
   const int per_head = n_qt - qt0;
-  const int steps = g * per_head;
+  const int n_diag = CAUSAL ? max(0, min(per_head, (k0 + C::kBKV - 2 - diag) / C::kBQ - qt0 + 1)) : 0;
+  const int n_rest = per_head - n_diag;
+  const int n_dsteps = g * n_diag;
+  const int steps = g * n_rest;
 
-  // Loads of step s into buffer buf.  A step past the end (valid false)
-  // issues the same instructions on empty ranges, which read nothing, so
-  // every step issues the same number of loads and needs no branch.
-  auto load_step = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
-    s = valid ? s : 0;
-    const int hq = hkv * g + s / per_head;
-    const int qt = qt0 + s % per_head;
-    const size_t bhq = (size_t)b * p.Hq + hq;
+  // Loads of query tile qt of head hh of the group into buffer buf.  An
+  // invalid tile issues the same instructions on empty ranges, which read
+  // nothing, so that no wave branches.
+  auto load_tile = [&](int hh, int qt, int buf, bool valid) __attribute__((always_inline)) {
+    const size_t bhq = (size_t)b * p.Hq + hkv * g + hh;
     const size_t q_slab = bhq * p.Nq * D;
     const uint32_t bytes = valid ? (uint32_t)p.Nq * C::kRowBytes : 0u;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * 2, bytes);
@@ -393,16 +387,23 @@ void bwd_dkdv16_kernel(DkvParams p) {
     const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
     dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, qbuf(buf), w, lane);
     dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, dobuf(buf), w, lane);
-    // The step's row statistics: wave 0 stages lse2 and wave 1 dsum, one
-    // 16-lane load each, so every wave's count of loads per step is exact.
-    if (w < 2 && lane < 16) {
-      const float* src = (w == 0 ? p.lse2 : p.dsum) + bhq * p.Nq;
-      buf_load16_to_lds(make_rsrc(src, valid ? (uint32_t)p.Nq * 4 : 0u), (uint32_t)qt * C::kBQ * 4 + lane * 16,
-                        stbuf(buf) + w * 256);
-    }
+    // Row statistics, one dword per lane: wave 0 stages lse2 and wave 1
+    // dsum; waves 2 and 3 load from an empty range into their own slots.
+    const float* src = (w == 0 ? p.lse2 : p.dsum) + bhq * p.Nq;
+    const uint32_t nb = (valid && w < 2) ? (uint32_t)p.Nq * 4 : 0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, nb), (lds_void*)(stbuf(buf) + w * 256), 4,
+                                             (uint32_t)qt * C::kBQ * 4 + lane * 4, 0, 0, 0);
   };
-  auto first_row = [&](int s) __attribute__((always_inline)) { return (qt0 + s % per_head) * C::kBQ; };
+  auto load_step = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
+    s = valid ? s : 0;
+    load_tile(s / n_rest, qt0 + n_diag + s % n_rest, buf, valid);
+  };
+  auto load_diag = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
+    s = valid ? s : 0;
+    load_tile(s / n_diag, qt0 + s % n_diag, buf, valid);
+  };
 
+  if (n_dsteps > 0) load_diag(0, 2, true);
   if (steps > 0) load_step(0, 0, true);
   if (steps > 1) load_step(1, 1, true);
 
@@ -417,6 +418,8 @@ void bwd_dkdv16_kernel(DkvParams p) {
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
+  // Per-lane LDS offsets: Q / dO row fragments (A rows are sigma-permuted
+  // queries), Qᵀ / dOᵀ column fragments, and this lane's rows of a stats area.
   uint32_t roff[KS], coff[DT][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) roff[ks] = F::template row_off<TT>(sigma(col), ks, h);
@@ -424,12 +427,7 @@ void bwd_dkdv16_kernel(DkvParams p) {
   for (int dt = 0; dt < DT; dt++)
 #pragma unroll
     for (int u = 0; u < 2; u++) coff[dt][u] = F::template col_off<TT>(32 * dt, u, lane);
-
-  // Buffer 3 stands for step -1 of the first phase A: zero it.
-  for (int i = threadIdx.x; i < C::kTileBytes / 16; i += 256) {
-    *(__attribute__((address_space(3))) u32x4*)(qbuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
-    *(__attribute__((address_space(3))) u32x4*)(dobuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
-  }
+  uint32_t soff = 32 * h;
 
   f32x16 sv[MT], dp[MT];
   Frag pa[PS], da[PS], pb[PS], db[PS];  // P and dS fragments of two consecutive steps
@@ -486,14 +484,146 @@ void bwd_dkdv16_kernel(DkvParams p) {
       }
   };
 
-  constexpr int kDmaPerStep =
-      2 * ((C::kBQ * C::kRowBytes / 1024) >= C::kWaves ? (C::kBQ * C::kRowBytes / 1024) / C::kWaves : 1);
+  // ---- Diagonal tiles (causal only), unpipelined, alternating between
+  // buffers 2 and 3; each step's barrier publishes its tiles and frees the
+  // other buffer for the next tile's loads.
+  auto diag_step = [&](auto bc, int s) __attribute__((always_inline)) {
+    constexpr int bi = decltype(bc)::value;
+    wait_vmem();
+    barrier_lds();
+    load_diag(s + 1, 5 - bi, s + 1 < n_dsteps);
+    gemm_sdp(qbuf(bi), dobuf(bi));
+    mask((qt0 + s % n_diag) * C::kBQ);
+    p_ds(stbuf(bi), pa, da);
+    gemm_dvdk(qbuf(bi), dobuf(bi), pa, da);
+  };
+  for (int s = 0; s < n_dsteps; s += 2) {
+    diag_step(Int<2>{}, s);
+    if (s + 1 < n_dsteps) diag_step(Int<3>{}, s + 1);
+  }
+  // Buffer 3 stands for step -1 of the first pipelined step: zero it once
+  // every wave is done with the diagonal tiles.
+  if (n_dsteps > 0) barrier_lds();
+  for (int i = threadIdx.x; i < C::kTileBytes / 16; i += 256) {
+    *(__attribute__((address_space(3))) u32x4*)(qbuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
+    *(__attribute__((address_space(3))) u32x4*)(dobuf(3) + 16 * i) = u32x4{0, 0, 0, 0};
+  }
 
-  // Step i (bi = i mod 4; P/dS of step i go to (pn, dn), those of step i-1 are (po, dob_)).
+  // ---- One pipelined step, as kNChunks chunks of kChunk products, each
+  // chunk fenced from the next.  Products 0 .. NA-1 are dVᵀ/dKᵀ of step i-1
+  // (ps, dt, dV then dK), products NA .. NA+NB-1 are S/dP of step i+1 (M tile
+  // mt, k block ks, S then dP).  The fragment of product m is read two
+  // products ahead.  P/dS of step i are cut into pieces (mt, u) of 8 queries
+  // and each piece into three stages; stage g (piece g/3) runs in chunk
+  // g * kChunkMt1 / (3 * kPieces), so that every piece of M tile mt is done
+  // before the chunk whose products overwrite tile mt's S and dP.
+  constexpr int NA = 2 * PS * DT, NB = 2 * KS * MT, NM = NA + NB;
+  constexpr int kChunk = 4, kLead = 2;
+  static_assert(NA % kChunk == 0 && (2 * KS) % kChunk == 0, "chunks hold whole product groups");
+  constexpr int kNChunks = NM / kChunk;
+  constexpr int kPieces = 2 * MT;
+  constexpr int kChunkMt1 = (NA + 2 * KS * (MT - 1)) / kChunk;  // first chunk of the last M tile's S/dP
+  constexpr auto stage_chunk = [](int g) constexpr { return g * kChunkMt1 / (3 * kPieces); };
+
+  auto fused = [&](const lds_char* stb, const lds_char* q_old, const lds_char* do_old, const lds_char* q_new,
+                   const lds_char* do_new, Frag (&pn)[PS], Frag (&dn)[PS], const Frag (&po)[PS],
+                   const Frag (&dq_)[PS]) __attribute__((always_inline)) {
+    float l2[kPieces][8], dd[kPieces][8], pv[kPieces][8], xv[kPieces][8];
+    auto read_a = [&](auto mc) __attribute__((always_inline)) -> Frag {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NA) {
+        constexpr int ps = m / (2 * DT), dt = (m % (2 * DT)) / 2, which = m % 2;
+        return F::lds_col_at((which ? q_old : do_old) + 16 * ps * C::kRowBytes, coff[dt][0], coff[dt][1]);
+      } else {
+        constexpr int j = m - NA, mt = j / (2 * KS), ks = (j % (2 * KS)) / 2, which = j % 2;
+        return F::lds_row_at((which ? do_new : q_new) + 32 * mt * C::kRowBytes, roff[ks]);
+      }
+    };
+    auto product = [&](auto mc, const Frag& a) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NA) {
+        constexpr int ps = m / (2 * DT), dt = (m % (2 * DT)) / 2, which = m % 2;
+        if constexpr (which == 0) dv[dt] = E::mma(a, po[ps], dv[dt]);
+        else dk[dt] = E::mma(a, dq_[ps], dk[dt]);
+      } else {
+        constexpr int j = m - NA, mt = j / (2 * KS), ks = (j % (2 * KS)) / 2, which = j % 2;
+        if constexpr (which == 0) sv[mt] = E::mma(a, kf[ks], ks == 0 ? f32x16{} : sv[mt]);
+        else dp[mt] = E::mma(a, vf[ks], ks == 0 ? f32x16{} : dp[mt]);
+      }
+    };
+    auto stats = [&](int pc) __attribute__((always_inline)) {
+      const lds_char* sb = stb + 4 * (32 * (pc / 2) + 16 * (pc % 2));
+      const u32x4 a0 = lds_read16(sb, soff), a1 = lds_read16(sb + 16, soff);
+      const u32x4 b0 = lds_read16(sb + 4 * C::kBQ, soff), b1 = lds_read16(sb + 4 * C::kBQ + 16, soff);
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        l2[pc][t] = as_float(a0[t]);
+        l2[pc][4 + t] = as_float(a1[t]);
+        dd[pc][t] = as_float(b0[t]);
+        dd[pc][4 + t] = as_float(b1[t]);
+      }
+    };
+    // Stage 0: c s - lse2; stage 1: P = exp2(.), dP - D; stage 2: dS, both
+    // packed, and the next piece's stats read.
+    auto stage = [&](auto gc) __attribute__((always_inline)) {
+      constexpr int gi = decltype(gc)::value, pc = gi / 3, st = gi % 3, mt = pc / 2, u = pc % 2;
+      if constexpr (st == 0) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) xv[pc][t] = fmaf(sv[mt][8 * u + t], c, -l2[pc][t]);
+      } else if constexpr (st == 1) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          pv[pc][t] = fast_exp2(xv[pc][t]);
+          xv[pc][t] = dp[mt][8 * u + t] - dd[pc][t];
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; t++) xv[pc][t] *= pv[pc][t];
+        pn[pc] = E::pack(pv[pc]);
+        dn[pc] = E::pack(xv[pc]);
+        if constexpr (pc + 1 < kPieces) stats(pc + 1);
+      }
+    };
+    Frag ra[kLead + 1];
+    stats(0);
+    static_for<0, kLead>([&](auto jc) __attribute__((always_inline)) {
+      ra[decltype(jc)::value] = read_a(Int<decltype(jc)::value>{});
+    });
+    static_for<0, kNChunks>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      static_for<0, kChunk>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int m = kChunk * k + decltype(jc)::value;
+        if constexpr (m + kLead < NM) ra[(m + kLead) % (kLead + 1)] = read_a(Int<m + kLead>{});
+        product(Int<m>{}, ra[m % (kLead + 1)]);
+      });
+      static_for<0, 3 * kPieces>([&](auto gc) __attribute__((always_inline)) {
+        if constexpr (stage_chunk(decltype(gc)::value) == k) stage(gc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Step i (bi = i mod 4): P/dS of step i go to (pn, dn); (po, dq_) hold
+  // those of step i-1.
   auto iter = [&](auto bc, Frag (&pn)[PS], Frag (&dn)[PS], const Frag (&po)[PS], const Frag (&dq_)[PS], int i)
       __attribute__((always_inline)) {
     constexpr int bi = decltype(bc)::value;
+    // Step i+1's tiles are this wave's only loads in flight; once they have
+    // landed in every wave, the barrier also frees the buffer of step i-2.
+    wait_vmem();
+    barrier_lds();
     load_step(i + 2, (bi + 2) & 3, i + 2 < steps);
+    // The lane offsets are hidden from the compiler anew every step: it then
+    // adds buffer bases within the step instead of keeping a register for
+    // every (buffer, offset) pair across the loop.
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) asm volatile("" : "+v"(roff[ks]));
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+      asm volatile("" : "+v"(coff[dt][0]));
+      asm volatile("" : "+v"(coff[dt][1]));
+    }
+    asm volatile("" : "+v"(soff));
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
       asm volatile("" : "+a"(dk[dt]));
@@ -504,24 +634,10 @@ void bwd_dkdv16_kernel(DkvParams p) {
       asm volatile("" : "+a"(kf[ks]));
       asm volatile("" : "+a"(vf[ks]));
     }
-    // Past the last step sv/dp hold stale values; their P/dS are never used.
-    if (CAUSAL && i < steps && kw + 31 > first_row(i) + diag) mask(first_row(i));
-    // Phase A.
-    p_ds(stbuf(bi), pn, dn);
-    gemm_dvdk(qbuf((bi + 3) & 3), dobuf((bi + 3) & 3), po, dq_);
-    sched_phase_a<4 * MT, 4 * PS * DT, 2 * PS * DT, 5, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    // Step i+1's loads (issued one step ago) must have landed; this step's
-    // loads (kDmaPerStep per wave, plus one stats load on waves 0 and 1) may
-    // stay in flight: loads retire in issue order.
-    if (w < 2) wait_vmem_le<kDmaPerStep + 1>();
-    else wait_vmem_le<kDmaPerStep>();
-    barrier_lds();
-    // Phase B.
-    if (i + 1 < steps) {
-      gemm_sdp(qbuf((bi + 1) & 3), dobuf((bi + 1) & 3));
-      sched_mfma_valu_reads<2 * KS * MT, 2 * KS * MT, 0, 4>();
-    }
+    // Past the last step S/dP read a stale buffer and P/dS are never used.
+    fused(stbuf(bi), qbuf((bi + 3) & 3), dobuf((bi + 3) & 3), qbuf((bi + 1) & 3), dobuf((bi + 1) & 3), pn, dn, po,
+          dq_);
   };
 
   wait_vmem();
@@ -782,10 +898,9 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
   p.c = a.scale * kLog2e; p.scale = a.scale;
   const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
-  // The pipelined kernel wins when every work-group walks all query tiles;
-  // under the causal mask most work-groups are short and the plain kernel,
-  // which has no pipeline to fill and drain, is faster.
-  if constexpr (Elem<T>::kBytes == 2 && !CAUSAL)
+  // 16-bit types take the pipelined kernel; float32 (whose fragments leave
+  // no registers for a pipeline) the plain one.
+  if constexpr (Elem<T>::kBytes == 2)
     hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);

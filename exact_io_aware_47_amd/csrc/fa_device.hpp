@@ -49,6 +49,15 @@ __device__ __forceinline__ float as_float(uint32_t x) { return __builtin_bit_cas
 // Compile-time integer as a value (selects unrolled variants in lambdas).
 template <int N> struct Int { static constexpr int value = N; };
 
+// fn(Int<B>{}), fn(Int<B + 1>{}), ..., fn(Int<E - 1>{}).
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (B < E) {
+    fn(Int<B>{});
+    static_for<B + 1, E>(fn);
+  }
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / 64); }
 
