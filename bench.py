@@ -245,7 +245,7 @@ def profile_once(torch, fa, si):
 
 COPY_BYTES = 1 << 30
 # rocprofv3 kernel names -> the keys used above (the decode is split + reduce).
-KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_kernel", "dkdv"),
+KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_kernel", "dkdv"), ("bwd_dkdv16_kernel", "dkdv"),
                ("bwd_dq_kernel", "dq"), ("decode_split_kernel", "decode"), ("decode_reduce_kernel", "decode"))
 
 
