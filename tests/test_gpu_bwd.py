@@ -52,6 +52,11 @@ CASES = [
     (1, 2, 2, 64, 64, 128, "f16", True),
     (3, 6, 3, 190, 190, 128, "f16", False),
     (1, 6, 2, 1000, 1000, 64, "bf16", True),
+    # causal with keys far beyond the queries (most key tiles need no mask),
+    # with more queries than keys, and with GQA over an offset diagonal
+    (1, 2, 2, 64, 1000, 128, "bf16", True),
+    (2, 4, 2, 700, 256, 64, "bf16", True),
+    (1, 3, 1, 200, 700, 128, "f16", True),
 ]
 
 
