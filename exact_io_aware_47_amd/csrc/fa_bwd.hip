@@ -394,13 +394,16 @@ void bwd_dkdv16_kernel(DkvParams p) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, nb), (lds_void*)(stbuf(buf) + w * 256), 4,
                                              (uint32_t)qt * C::kBQ * 4 + lane * 4, 0, 0, 0);
   };
+  // (An invalid step maps to tile 0 of head 0; the divisors are kept
+  // nonzero for the calls that load nothing.)
+  const int n_rest_d = max(n_rest, 1), n_diag_d = max(n_diag, 1);
   auto load_step = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
     s = valid ? s : 0;
-    load_tile(s / n_rest, qt0 + n_diag + s % n_rest, buf, valid);
+    load_tile(s / n_rest_d, qt0 + n_diag + s % n_rest_d, buf, valid);
   };
   auto load_diag = [&](int s, int buf, bool valid) __attribute__((always_inline)) {
     s = valid ? s : 0;
-    load_tile(s / n_diag, qt0 + s % n_diag, buf, valid);
+    load_tile(s / n_diag_d, qt0 + s % n_diag_d, buf, valid);
   };
 
   if (n_dsteps > 0) load_diag(0, 2, true);
@@ -493,7 +496,7 @@ void bwd_dkdv16_kernel(DkvParams p) {
     barrier_lds();
     load_diag(s + 1, 5 - bi, s + 1 < n_dsteps);
     gemm_sdp(qbuf(bi), dobuf(bi));
-    mask((qt0 + s % n_diag) * C::kBQ);
+    mask((qt0 + s % n_diag_d) * C::kBQ);
     p_ds(stbuf(bi), pa, da);
     gemm_dvdk(qbuf(bi), dobuf(bi), pa, da);
   };
