@@ -270,27 +270,6 @@ __device__ __forceinline__ void sched_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(kMaskMfma, pd, 0);
 }
 
-// Interleave a block of MFMAs with their LDS fragment reads and with
-// independent VALU work: NR reads feed NM MFMAs in order.  The reads of the
-// first PD MFMAs are issued up front; then each MFMA is followed by up to NV
-// VALU instructions (transcendentals included) and by the reads of the MFMA
-// PD places later.
-template <int NR, int NM, int NV, int PD, int I = 0>
-__device__ __forceinline__ void sched_mfma_valu_reads() {
-  constexpr int kMfma = 0x008, kValu = 0x002 | 0x400, kDsRead = 0x100;
-  static_assert(NR % NM == 0 || NM % NR == 0, "reads and MFMAs must divide");
-  constexpr auto need = [](int i) constexpr { return (i * NR + NM - 1) / NM; };  // reads of the first i MFMAs
-  constexpr int pd = PD < NM ? PD : NM;
-  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, need(pd), 0);
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(kValu, NV, 0);
-    constexpr int lo = need(I + pd < NM ? I + pd : NM), hi = need(I + 1 + pd < NM ? I + 1 + pd : NM);
-    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(kDsRead, hi - lo, 0);
-    sched_mfma_valu_reads<NR, NM, NV, PD, I + 1>();
-  }
-}
-
 // --------------------------------------------------------------------------
 // Cross-lane helpers
 // --------------------------------------------------------------------------
