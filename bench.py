@@ -123,8 +123,8 @@ def ensure_library():
         build.build()
 
 
-def bench_training(torch, fa, si, steps, warmup):
-    w = si.WORKLOADS["mha_bf16_4k"]
+def bench_training(torch, fa, si, steps, warmup, name="mha_bf16_4k"):
+    w = si.WORKLOADS[name]
     q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
@@ -382,6 +382,12 @@ def main(argv=None):
                    "arch": getattr(props, "gcnArchName", "")},
         "host_wall_s_timed": round(wall, 4),
     }
+    # The grouped-query training shape (four query heads per K/V head), same step.
+    wg, ms_g, per_g, _ = bench_training(torch, fa, si, args.steps, args.warmup, "gqa_bf16_4k")
+    flg = attention_flops(wg.B, wg.Hq, wg.Nq, wg.Nk, wg.d, True)
+    line["gqa"] = {"workload": "gqa_bf16_4k: causal forward + backward, B=2 Hq=32 Hkv=8 N=4096 d=128 bf16",
+                   "TFLOP/s": round((flg["fwd"] + flg["dkdv"] + flg["dq"]) / (ms_g * 1e-3) / 1e12, 2),
+                   "ms_per_step": round(ms_g, 4), "us": {n: round(v * 1e3, 2) for n, v in per_g.items()}}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)

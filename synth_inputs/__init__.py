@@ -15,6 +15,8 @@ configurations; the pages themselves publish no inputs or seeds):
 * ``mha_bf16_16k``    B=1  H=16 N=16384  d=128 bf16, causal, Q and K times 8
 * ``decode_gqa_paged`` B=8 Hq=32 Hkv=8 Nk=32768 d=128 bf16, 16-token pages
   reached through a seeded random permutation block table.
+* ``gqa_bf16_4k``     B=2 Hq=32 Hkv=8 N=4096 d=128 bf16, causal (grouped-query
+  training shape; not one of the five configurations)
 
 Draw order for a forward/backward workload: Q, K, V, dO, each i.i.d. N(0, 1)
 from ``torch.Generator('cpu').manual_seed(seed)``.  For decode: Q, K cache,
@@ -92,6 +94,8 @@ WORKLOADS = {
     "mha_bf16_16k": AttnWorkload("mha_bf16_16k", 1, 16, 16, 16384, 16384, 128, "bf16", (True,), 47004,
                                  qk_mult=8.0),
     "decode_gqa_paged": DecodeWorkload("decode_gqa_paged", 8, 32, 8, 32768, 128, "bf16", 47005),
+    # grouped-query training shape: four query heads per K/V head
+    "gqa_bf16_4k": AttnWorkload("gqa_bf16_4k", 2, 32, 8, 4096, 4096, 128, "bf16", (True,), 47006),
 }
 
 

@@ -104,6 +104,22 @@ def test_bwd_workload_mha_bf16_4k():
     _sampled_heads(si.WORKLOADS["mha_bf16_4k"], [(0, 0), (1, 13)])
 
 
+def test_bwd_workload_gqa_bf16_4k():
+    """Grouped heads at the training shape: dK/dV of one K/V head are the sum
+    over its four query heads, so the oracle takes the whole group."""
+    w = si.WORKLOADS["gqa_bf16_4k"]
+    q, k, v, do = si.workload_attention_inputs(w)
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, True)
+    g = w.Hq // w.Hkv
+    b, hkv = 1, 5
+    qs = (slice(b, b + 1), slice(hkv * g, (hkv + 1) * g))
+    ks = (slice(b, b + 1), slice(hkv, hkv + 1))
+    rq, rk, rv = orc.attention_bwd(f64(q[qs]), f64(k[ks]), f64(v[ks]), f64(do[qs]), w.scale, True)
+    assert_close(f"dQ[{b},group {hkv}]", f64(dq[qs]), rq, w.dtype, "grad")
+    assert_close(f"dK[{b},{hkv}]", f64(dk[ks]), rk, w.dtype, "grad")
+    assert_close(f"dV[{b},{hkv}]", f64(dv[ks]), rv, w.dtype, "grad")
+
+
 def test_bwd_workload_mha_bf16_16k():
     dq, dk, dv = _sampled_heads(si.WORKLOADS["mha_bf16_16k"], [(0, 5)])
     for t in (dq, dk, dv):

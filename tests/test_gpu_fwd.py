@@ -117,6 +117,11 @@ def test_fwd_workload_mha_bf16_4k():
     _sampled_heads_check(w, [(0, 0), (1, 15), (0, 9)])
 
 
+def test_fwd_workload_gqa_bf16_4k():
+    w = si.WORKLOADS["gqa_bf16_4k"]
+    _sampled_heads_check(w, [(0, 0), (1, 22)])
+
+
 def test_fwd_workload_mha_bf16_16k():
     w = si.WORKLOADS["mha_bf16_16k"]
     rng = np.random.default_rng(5)
