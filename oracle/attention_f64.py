@@ -34,7 +34,16 @@ design notes):
 * a row with no visible key has O = 0, LSE = -inf and zero gradients;
 * grouped-query heads are contiguous groups: kv head = q head // (Hq / Hkv);
 * LSE = m + ln(l) in natural log;
-* KV cache pages are laid out [num_blocks, Hkv, block_size, d].
+* KV cache pages are laid out [num_blocks, Hkv, block_size, d];
+* a packed (variable-length) batch stores sequence b's rows of every head as
+  one [H, n_b, d] block starting at row H * cu[b]; each sequence is attended
+  on its own.
+* Packed batches: the related-work page's repository comparison (varlen
+  support in the reference implementation), the concept page's key
+  observation 4 (variable-length packing) and the tutorial's validation
+  checklist (variable-length sequences).  The pages give no layout; the
+  oracle splits the packed arrays into sequences and applies the dense
+  definition to each.
 
 Every function here is pinned in ``tests/test_oracle.py`` against values and
 properties that the pages and the mathematics fix.
@@ -52,6 +61,8 @@ __all__ = [
     "attention_fwd",
     "attention_bwd",
     "decode_paged",
+    "attention_fwd_packed",
+    "attention_bwd_packed",
     "gather_pages",
     "online_softmax_stats",
     "merge_softmax_stats",
@@ -155,6 +166,50 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool, row_ids=None, nq_tota
             dq[b, h] = scale * (ds @ kh)
             dk[b, h // g] += scale * (ds.T @ q[b, h])
             dv[b, h // g] += p.T @ do[b, h]
+    return dq, dk, dv
+
+
+def _unpack(x, cu, h: int, b: int):
+    """Sequence b of a packed [sum_b h*n_b, d] array as [1, h, n_b, d]."""
+    n = int(cu[b + 1]) - int(cu[b])
+    r0 = h * int(cu[b])
+    return x[r0:r0 + h * n].reshape(1, h, n, x.shape[-1])
+
+
+def attention_fwd_packed(q, k, v, cu_q, cu_k, hq: int, hkv: int, scale: float, causal: bool):
+    """Forward of a packed batch: each sequence through attention_fwd.
+    Returns O like q and LSE [sum_b hq*n_b] (float64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    o = np.zeros_like(q)
+    lse = np.zeros(q.shape[0])
+    for b in range(len(cu_q) - 1):
+        nq = int(cu_q[b + 1]) - int(cu_q[b])
+        if nq == 0:
+            continue
+        ob, lb = attention_fwd(_unpack(q, cu_q, hq, b), _unpack(k, cu_k, hkv, b), _unpack(v, cu_k, hkv, b),
+                               scale, causal)
+        r0 = hq * int(cu_q[b])
+        o[r0:r0 + hq * nq] = ob.reshape(hq * nq, -1)
+        lse[r0:r0 + hq * nq] = lb.reshape(-1)
+    return o, lse
+
+
+def attention_bwd_packed(q, k, v, do, cu_q, cu_k, hq: int, hkv: int, scale: float, causal: bool):
+    """Backward of a packed batch: each sequence through attention_bwd.
+    Returns dQ, dK, dV with the packed shapes of q, k, v (float64)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        nq = int(cu_q[b + 1]) - int(cu_q[b])
+        nk = int(cu_k[b + 1]) - int(cu_k[b])
+        if nq == 0 or nk == 0:
+            continue
+        gq, gk, gv = attention_bwd(_unpack(q, cu_q, hq, b), _unpack(k, cu_k, hkv, b), _unpack(v, cu_k, hkv, b),
+                                   _unpack(do, cu_q, hq, b), scale, causal)
+        rq, rk = hq * int(cu_q[b]), hkv * int(cu_k[b])
+        dq[rq:rq + hq * nq] = gq.reshape(hq * nq, -1)
+        dk[rk:rk + hkv * nk] = gk.reshape(hkv * nk, -1)
+        dv[rk:rk + hkv * nk] = gv.reshape(hkv * nk, -1)
     return dq, dk, dv
 
 

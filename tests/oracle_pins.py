@@ -373,7 +373,59 @@ def pin_large_logits_stable(orc):
     assert (gap >= -1e-12).all() and (gap <= math.log(64) + 1e-12).all()
 
 
+def pin_packed_equal_lengths_equals_dense(orc):
+    """A packed batch of equal-length sequences is the dense batch, flattened."""
+    rng = _rng(31)
+    b, hq, hkv, n, d = 3, 4, 2, 9, 4
+    q, k, v, do = _rand(rng, b, hq, n, d), _rand(rng, b, hkv, n, d), _rand(rng, b, hkv, n, d), _rand(rng, b, hq, n, d)
+    cu = np.arange(b + 1) * n
+    for causal in (False, True):
+        o, lse = orc.attention_fwd(q, k, v, 0.7, causal)
+        op, lp = orc.attention_fwd_packed(q.reshape(-1, d), k.reshape(-1, d), v.reshape(-1, d), cu, cu, hq, hkv, 0.7,
+                                          causal)
+        assert np.abs(op - o.reshape(-1, d)).max() == 0 and np.abs(lp - lse.reshape(-1)).max() == 0
+        g = orc.attention_bwd(q, k, v, do, 0.7, causal)
+        gp = orc.attention_bwd_packed(q.reshape(-1, d), k.reshape(-1, d), v.reshape(-1, d), do.reshape(-1, d), cu, cu,
+                                      hq, hkv, 0.7, causal)
+        for a, c in zip(gp, g):
+            assert np.abs(a - c.reshape(-1, d)).max() == 0
+
+
+def pin_packed_mixed_lengths(orc):
+    """Sequences of different query and key lengths (one empty), packed as
+    [H, n_b, d] blocks one after another: every block of the result is the
+    dense result of that sequence alone, and the other rows stay untouched."""
+    rng = _rng(32)
+    hq, hkv, d = 4, 2, 4
+    lq, lk = [5, 0, 11, 3], [7, 4, 11, 1]
+    seqs = [(_rand(rng, 1, hq, a, d), _rand(rng, 1, hkv, c, d), _rand(rng, 1, hkv, c, d), _rand(rng, 1, hq, a, d))
+            for a, c in zip(lq, lk)]
+    pack = lambda xs: np.concatenate([x[0].reshape(-1, d) for x in xs], axis=0)
+    q, k, v, do = (pack([s_[i] for s_ in seqs]) for i in range(4))
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    for causal in (False, True):
+        o, lse = orc.attention_fwd_packed(q, k, v, cu_q, cu_k, hq, hkv, 0.6, causal)
+        dq, dk, dv = orc.attention_bwd_packed(q, k, v, do, cu_q, cu_k, hq, hkv, 0.6, causal)
+        for bi, (qs, ks, vs, dos) in enumerate(seqs):
+            rq, rk = slice(hq * cu_q[bi], hq * cu_q[bi + 1]), slice(hkv * cu_k[bi], hkv * cu_k[bi + 1])
+            if lq[bi] == 0:
+                assert o[rq].size == 0
+                continue
+            ob, lb = orc.attention_fwd(qs, ks, vs, 0.6, causal)
+            # (rows that see no key carry LSE = -inf on both sides)
+            assert np.array_equal(o[rq], ob.reshape(-1, d)) and np.array_equal(lse[rq], lb.reshape(-1))
+            gb = orc.attention_bwd(qs, ks, vs, dos, 0.6, causal)
+            assert np.array_equal(dq[rq], gb[0].reshape(-1, d))
+            assert np.array_equal(dk[rk], gb[1].reshape(-1, d))
+            assert np.array_equal(dv[rk], gb[2].reshape(-1, d))
+        # the empty query sequence's keys get zero gradients
+        rk1 = slice(hkv * cu_k[1], hkv * cu_k[2])
+        assert np.abs(dk[rk1]).max() == 0 and np.abs(dv[rk1]).max() == 0
+
+
 ALL_PINS = [
+    pin_packed_equal_lengths_equals_dense,
+    pin_packed_mixed_lengths,
     pin_worked_example_streaming,
     pin_worked_example_attention,
     pin_rows_sum_to_one,

@@ -50,6 +50,11 @@ MUTANTS = [
     ("streaming sum not rescaled", "l = l * rescale + float", "l = l + float"),
     ("streaming block sum at old max", "float(np.exp(blk - m_new).sum())", "float(np.exp(blk - max(m, float(blk.max()) - 1.0) + 0 * m_new).sum())"),
     ("merge weights swapped", "return mx, l_a * wa + l_b * wb", "return mx, l_a * wb + l_b * wa"),
+    ("packed rows without head factor", "    r0 = h * int(cu[b])\n", "    r0 = int(cu[b])\n"),
+    ("packed blocks token-major", "return x[r0:r0 + h * n].reshape(1, h, n, x.shape[-1])",
+     "return x[r0:r0 + h * n].reshape(1, n, h, x.shape[-1]).transpose(0, 2, 1, 3)"),
+    ("packed dK rows at query offsets", "rq, rk = hq * int(cu_q[b]), hkv * int(cu_k[b])",
+     "rq, rk = hq * int(cu_q[b]), hkv * int(cu_q[b])"),
 ]
 
 
