@@ -163,6 +163,40 @@ def bench_training(torch, fa, si, steps, warmup, name="mha_bf16_4k"):
     return w, total_ms / steps, per, wall
 
 
+def bench_varlen(torch, fa, si, steps, warmup):
+    """Forward + backward of the packed variable-length workload; the backward
+    runs as one flash_attn_bwd_varlen call.  Returns (workload, lengths,
+    ms per step, {fwd, bwd: ms})."""
+    w = si.WORKLOADS["varlen_bf16"]
+    q, k, v, do, cu_q, cu_k = (t.to("cuda") for t in si.workload_packed_inputs(w))
+    lens = (cu_q[1:] - cu_q[:-1]).tolist()
+    mx = max(lens)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    tq = q.shape[0] // w.Hq
+    ws = torch.empty(fa.bwd_varlen_workspace_bytes(w.B, w.Hq, w.Hkv, tq, tq, mx, mx, w.d, fa.FA_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        fa.fwd_varlen(q, k, v, cu_q, cu_k, w.Hq, w.Hkv, mx, mx, causal=w.causal, out=o, lse=lse)
+        if ev: ev[1].record()
+        fa.bwd_varlen(q, k, v, o, do, lse, cu_q, cu_k, w.Hq, w.Hkv, mx, mx, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                      workspace=ws)
+        if ev: ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(("fwd", "bwd"))}
+    return w, lens, per["fwd"] + per["bwd"], per
+
+
 def bench_decode(torch, fa, si, steps, warmup):
     w = si.WORKLOADS["decode_gqa_paged"]
     q, kc, vc, table, lens = (t.to("cuda") for t in si.workload_decode_inputs(w))
@@ -388,6 +422,19 @@ def main(argv=None):
     line["gqa"] = {"workload": "gqa_bf16_4k: causal forward + backward, B=2 Hq=32 Hkv=8 N=4096 d=128 bf16",
                    "TFLOP/s": round((flg["fwd"] + flg["dkdv"] + flg["dq"]) / (ms_g * 1e-3) / 1e12, 2),
                    "ms_per_step": round(ms_g, 4), "us": {n: round(v * 1e3, 2) for n, v in per_g.items()}}
+    # Packed variable-length batch (16 causal sequences of seeded lengths), same step.
+    wv, lens_v, ms_v, per_v = bench_varlen(torch, fa, si, args.steps, args.warmup)
+    flv = {"fwd": 0, "dkdv": 0, "dq": 0}
+    for n in lens_v:
+        for key, val in attention_flops(1, wv.Hq, n, n, wv.d, wv.causal).items():
+            flv[key] += val
+    line["varlen"] = {"workload": f"varlen_bf16: packed batch of {wv.B} causal sequences, Hq=Hkv={wv.Hq}, d={wv.d} "
+                                  f"bf16, {sum(lens_v)} tokens, lengths uniform in [1, {wv.max_len}]",
+                      "lengths": lens_v, "seed": wv.seed,
+                      "TFLOP/s": round((flv["fwd"] + flv["dkdv"] + flv["dq"]) / (ms_v * 1e-3) / 1e12, 2),
+                      "fwd_tflops": round(flv["fwd"] / (per_v["fwd"] * 1e-3) / 1e12, 2),
+                      "bwd_tflops": round((flv["dkdv"] + flv["dq"]) / (per_v["bwd"] * 1e-3) / 1e12, 2),
+                      "ms_per_step": round(ms_v, 4), "us": {n: round(v * 1e3, 2) for n, v in per_v.items()}}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)

@@ -38,6 +38,10 @@ SIGNATURES = {
     "flash_attn_bwd_preprocess": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "flash_attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "flash_attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "flash_attn_bwd_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "flash_attn_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "flash_attn_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -175,6 +179,64 @@ def bwd_phase(phase: str, q, k, v, out, dout, lse, dq, dk, dv, workspace, causal
     else:
         raise ValueError(f"unknown backward phase {phase!r}")
     _check(code, f"flash_attn_bwd_{phase}")
+
+
+def _packed(q, k, cu_q, cu_k, hq, hkv, max_seqlen_q, max_seqlen_k):
+    """Sizes of a packed batch: q [hq*total_q, d], k [hkv*total_k, d], cu_* [B+1] int32."""
+    _dense("q", q, ndim=2)
+    _dense("k", k, q.dtype, 2)
+    _dense("cu_q", cu_q, torch.int32, 1)
+    _dense("cu_k", cu_k, torch.int32, 1)
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError(f"cu_q and cu_k must both have B + 1 >= 2 entries, got {cu_q.numel()} and {cu_k.numel()}")
+    if q.shape[0] % hq or k.shape[0] % hkv or q.shape[1] != k.shape[1]:
+        raise ValueError(f"packed shapes q {tuple(q.shape)} / k {tuple(k.shape)} do not match Hq={hq}, Hkv={hkv}")
+    return cu_q.numel() - 1, q.shape[0] // hq, k.shape[0] // hkv, q.shape[1], int(max_seqlen_q), int(max_seqlen_k)
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, hq: int, hkv: int, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+               scale=None, out=None, lse=None):
+    """O, LSE of a packed batch.  q [hq*total_q, d]; k, v [hkv*total_k, d];
+    head h of sequence b occupies rows H*cu[b] + h*n_b ... (+ n_b)."""
+    B, tq, tk, d, mq, mk = _packed(q, k, cu_q, cu_k, hq, hkv, max_seqlen_q, max_seqlen_k)
+    _dense("v", v, q.dtype, 2)
+    if v.shape != k.shape:
+        raise ValueError(f"v shape {tuple(v.shape)} does not match k {tuple(k.shape)}")
+    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
+    lse = torch.empty(q.shape[0], dtype=torch.float32, device=q.device) if lse is None else \
+        _dense("lse", lse, torch.float32)
+    code = lib().flash_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
+                                       B, hq, hkv, tq, tk, mq, mk, d, _default_scale(d, scale), int(bool(causal)),
+                                       _dtype_code(q), _stream(q.device))
+    _check(code, "flash_attn_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen_workspace_bytes(B, hq, hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, dtype_code) -> int:
+    return int(lib().flash_attn_bwd_varlen_workspace_bytes(B, hq, hkv, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                                           d, dtype_code))
+
+
+def bwd_varlen(q, k, v, out, dout, lse, cu_q, cu_k, hq: int, hkv: int, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of a packed batch (layout as in fwd_varlen)."""
+    B, tq, tk, d, mq, mk = _packed(q, k, cu_q, cu_k, hq, hkv, max_seqlen_q, max_seqlen_k)
+    for name, t in (("v", v), ("out", out), ("dout", dout)):
+        _dense(name, t, q.dtype, 2)
+    _dense("lse", lse, torch.float32, 1)
+    dq = torch.empty_like(q) if dq is None else _dense("dq", dq, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _dense("dk", dk, q.dtype)
+    dv = torch.empty_like(v) if dv is None else _dense("dv", dv, q.dtype)
+    code_dt = _dtype_code(q)
+    ws_bytes = bwd_varlen_workspace_bytes(B, hq, hkv, tq, tk, mq, mk, d, code_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    code = lib().flash_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), B, hq, hkv, tq, tk, mq, mk, d,
+                                       _default_scale(d, scale), int(bool(causal)), code_dt, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "flash_attn_bwd_varlen")
+    return dq, dk, dv
 
 
 def decode_num_splits(B, Hkv, max_blocks_per_seq, block_size=16) -> int:

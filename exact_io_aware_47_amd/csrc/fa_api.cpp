@@ -30,6 +30,24 @@ int check_dense(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int 
   return FA_OK;
 }
 
+// Checks of the packed (variable-length) entry points, in the documented order.
+int check_varlen(int B, int Hq, int Hkv, int total_q, int total_k, int max_q, int max_k, int d, float scale,
+                 int dtype) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0 || max_q > total_q ||
+      max_k > total_k)
+    return FA_ERR_SHAPE;
+  if (!headdim_ok(d)) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if ((int64_t)Hq * total_q * d >= kMaxElems || (int64_t)Hkv * total_k * d >= kMaxElems) return FA_ERR_SHAPE;
+  // Grids span (sequence, head, tile of the longest sequence); keep them and B + 1 in 32 bits.
+  if ((int64_t)B * Hq * ((max_q + 127) / 128 + 1) >= kMaxElems ||
+      (int64_t)B * Hkv * ((max_k + 127) / 128 + 1) >= kMaxElems)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
@@ -66,6 +84,23 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
   a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
+int flash_attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens_q,
+                          const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                          int max_seqlen_k, int d, float scale, int causal, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  const int st = check_varlen(B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = max_seqlen_q; a.Nk = max_seqlen_k; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.tot_q = total_q; a.tot_k = total_k;
   return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -137,6 +172,37 @@ int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* d
   if (!Q || !K || !V || !dO || !dQ) return FA_ERR_NULL;
   const BwdPtrs t = {Q, K, V, nullptr, dO, nullptr, dQ, nullptr, nullptr, workspace};
   return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdDq, stream);
+}
+
+size_t flash_attn_bwd_varlen_workspace_bytes(int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                                             int max_seqlen_k, int d, int dtype) {
+  if (check_varlen(B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, 1.0f, dtype) != FA_OK) return 0;
+  return 2 * (size_t)Hq * total_q * sizeof(float);  // D row terms, then LSE * log2(e)
+}
+
+int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, void* dQ, void* dK, void* dV, const int* cu_seqlens_q,
+                          const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                          int max_seqlen_k, int d, float scale, int causal, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_NULL;
+  const int st = check_varlen(B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = flash_attn_bwd_varlen_workspace_bytes(B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                                            d, dtype);
+  if ((need > 0 && !workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* dense[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
+  for (const void* p : dense)
+    if (p && !aligned(p, 16)) return FA_ERR_ALIGN;
+  if (!aligned(LSE, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4)) return FA_ERR_ALIGN;
+  fa::BwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
+  a.dq = dQ; a.dk = dK; a.dv = dV; a.dsum = (float*)workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = max_seqlen_q; a.Nk = max_seqlen_k; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.tot_q = total_q; a.tot_k = total_k;
+  return launch_status(fa::launch_bwd(a, fa::kBwdAll, (hipStream_t)stream));
 }
 
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {

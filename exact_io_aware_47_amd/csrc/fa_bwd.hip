@@ -88,8 +88,10 @@ struct DkvParams {
   const float* dsum;
   void* dk;
   void* dv;
-  int B, Hq, Hkv, Nq, Nk;
-  int n_ktiles;
+  const int* cu_q;  // packed batch: cumulative query / key counts [B + 1], else null
+  const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk;  // Nq, Nk: the lengths (dense) or their bounds (packed)
+  int tot_q, tot_k;        // packed batch: total query / key tokens
   float c;      // scale * log2(e)
   float scale;
 };
@@ -128,20 +130,27 @@ void bwd_dkdv_kernel(DkvParams p) {
   const int kt = id / bh_count;
   const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
   const int g = p.Hq / p.Hkv;
+  // The grid covers the longest sequence; blocks past a shorter one's keys leave at once.
+  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  const int Nq = sr.nq, Nk = sr.nk;
+  if (kt * C::kBKV >= Nk) return;
+  const size_t kv_row0 = (size_t)p.Hkv * sr.tk + (size_t)hkv * Nk;  // first row of this (sequence, kv head)
+  // First row of query head hq of this sequence (in Q, dO and the row terms).
+  auto q_row0 = [&](int hq) __attribute__((always_inline)) { return (size_t)p.Hq * sr.tq + (size_t)hq * Nq; };
 
   const int lane = lane_id(), w = wave_id();
   const int h = lane >> 5, col = lane & 31;
   const int k0 = kt * C::kBKV;
   const int kw = k0 + 32 * w;   // first key of this wave
   const int key = kw + col;     // this lane's key
-  const int diag = p.Nk - p.Nq; // key j is visible to row i iff j <= i + diag (causal)
+  const int diag = Nk - Nq; // key j is visible to row i iff j <= i + diag (causal)
 
-  const size_t kv_slab = (size_t)bhk * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const size_t kv_slab = kv_row0 * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
 
   // Query tiles that can see this work-group's keys, for each head of the group.
-  const int n_qt = (p.Nq + C::kBQ - 1) / C::kBQ;
+  const int n_qt = (Nq + C::kBQ - 1) / C::kBQ;
   const int qt0 = CAUSAL ? max(0, k0 - diag) / C::kBQ : 0;
   const int per_head = n_qt - qt0;
   const int steps = g * per_head;
@@ -149,10 +158,10 @@ void bwd_dkdv_kernel(DkvParams p) {
   auto load_step = [&](int s, int buf) __attribute__((always_inline)) {
     const int hq = hkv * g + s / per_head;
     const int qt = qt0 + s % per_head;
-    const size_t bhq = (size_t)b * p.Hq + hq;
-    const size_t q_slab = bhq * p.Nq * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+    const size_t qr0 = q_row0(hq);
+    const size_t q_slab = qr0 * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
     const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
     dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rq, g0, buf ? qbuf(1) : qbuf(0), w, lane);
     dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, buf ? dobuf(1) : dobuf(0), w, lane);
@@ -160,8 +169,8 @@ void bwd_dkdv_kernel(DkvParams p) {
     if (w == 0) {
       const uint32_t off = (uint32_t)qt * C::kBQ * 4 + (lane & 15) * 16;
       lds_char* st = buf ? stbuf(1) : stbuf(0);
-      if (lane < 16) buf_load16_to_lds(make_rsrc(p.lse2 + bhq * p.Nq, (uint32_t)p.Nq * 4), off, st);
-      else if (lane < 32) buf_load16_to_lds(make_rsrc(p.dsum + bhq * p.Nq, (uint32_t)p.Nq * 4), off, st);
+      if (lane < 16) buf_load16_to_lds(make_rsrc(p.lse2 + qr0, (uint32_t)Nq * 4), off, st);
+      else if (lane < 32) buf_load16_to_lds(make_rsrc(p.dsum + qr0, (uint32_t)Nq * 4), off, st);
     }
   };
 
@@ -286,8 +295,8 @@ void bwd_dkdv_kernel(DkvParams p) {
   }
 
   // ---- epilogue: dK = scale * dKᵀ acc, dV; lane's column is its key.
-  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++)
 #pragma unroll
@@ -350,24 +359,31 @@ void bwd_dkdv16_kernel(DkvParams p) {
   const int kt = id / bh_count;
   const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
   const int g = p.Hq / p.Hkv;
+  // The grid covers the longest sequence; blocks past a shorter one's keys leave at once.
+  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  const int Nq = sr.nq, Nk = sr.nk;
+  if (kt * C::kBKV >= Nk) return;
+  const size_t kv_row0 = (size_t)p.Hkv * sr.tk + (size_t)hkv * Nk;  // first row of this (sequence, kv head)
+  // First row of query head hq of this sequence (in Q, dO and the row terms).
+  auto q_row0 = [&](int hq) __attribute__((always_inline)) { return (size_t)p.Hq * sr.tq + (size_t)hq * Nq; };
 
   const int lane = lane_id(), w = wave_id();
   const int h = lane >> 5, col = lane & 31;
   const int k0 = kt * C::kBKV;
   const int kw = k0 + 32 * w;
   const int key = kw + col;
-  const int diag = p.Nk - p.Nq;
+  const int diag = Nk - Nq;
   const bool neg = p.c < 0.f;
   const float c = neg ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
 
-  const size_t kv_slab = (size_t)bhk * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+  const size_t kv_slab = kv_row0 * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
 
   // Query tiles per head that see this work-group's keys: the first n_diag
   // of them cross the causal diagonal (every later row sees all 128 keys),
   // the other n_rest form the pipelined steps, head after head.
-  const int n_qt = (p.Nq + C::kBQ - 1) / C::kBQ;
+  const int n_qt = (Nq + C::kBQ - 1) / C::kBQ;
   const int qt0 = CAUSAL ? max(0, k0 - diag) / C::kBQ : 0;
   const int per_head = n_qt - qt0;
   const int n_diag = CAUSAL ? max(0, min(per_head, (k0 + C::kBKV - 2 - diag) / C::kBQ - qt0 + 1)) : 0;
@@ -379,9 +395,9 @@ void bwd_dkdv16_kernel(DkvParams p) {
   // invalid tile issues the same instructions on empty ranges, which read
   // nothing, so that no wave branches.
   auto load_tile = [&](int hh, int qt, int buf, bool valid) __attribute__((always_inline)) {
-    const size_t bhq = (size_t)b * p.Hq + hkv * g + hh;
-    const size_t q_slab = bhq * p.Nq * D;
-    const uint32_t bytes = valid ? (uint32_t)p.Nq * C::kRowBytes : 0u;
+    const size_t qr0 = q_row0(hkv * g + hh);
+    const size_t q_slab = qr0 * D;
+    const uint32_t bytes = valid ? (uint32_t)Nq * C::kRowBytes : 0u;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * 2, bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * 2, bytes);
     const uint32_t g0 = (uint32_t)qt * C::kBQ * C::kRowBytes;
@@ -389,8 +405,8 @@ void bwd_dkdv16_kernel(DkvParams p) {
     dma_tile<C::kRowBytes, C::kBQ, C::kWaves>(rdo, g0, dobuf(buf), w, lane);
     // Row statistics, one dword per lane: wave 0 stages lse2 and wave 1
     // dsum; waves 2 and 3 load from an empty range into their own slots.
-    const float* src = (w == 0 ? p.lse2 : p.dsum) + bhq * p.Nq;
-    const uint32_t nb = (valid && w < 2) ? (uint32_t)p.Nq * 4 : 0u;
+    const float* src = (w == 0 ? p.lse2 : p.dsum) + qr0;
+    const uint32_t nb = (valid && w < 2) ? (uint32_t)Nq * 4 : 0u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, nb), (lds_void*)(stbuf(buf) + w * 256), 4,
                                              (uint32_t)qt * C::kBQ * 4 + lane * 4, 0, 0, 0);
   };
@@ -658,8 +674,8 @@ void bwd_dkdv16_kernel(DkvParams p) {
   if (i + 1 <= steps) iter(Int<1>{}, pa, da, pb, db, i + 1);
   if (i + 2 <= steps) iter(Int<2>{}, pb, db, pa, da, i + 2);
 
-  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * 2, (uint32_t)p.Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wk = make_rsrc((char*)p.dk + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wv = make_rsrc((char*)p.dv + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
 #pragma unroll
   for (int dt = 0; dt < DT; dt++)
 #pragma unroll
@@ -696,8 +712,10 @@ struct DqParams {
   const float* lse2;
   const float* dsum;
   void* dq;
-  int B, Hq, Hkv, Nq, Nk;
-  int n_qtiles;
+  const int* cu_q;  // packed batch: cumulative query / key counts [B + 1], else null
+  const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk;  // Nq, Nk: the lengths (dense) or their bounds (packed)
+  int tot_q, tot_k;        // packed batch: total query / key tokens
   float c;
   float scale;
 };
@@ -717,32 +735,39 @@ void bwd_dq_kernel(DqParams p) {
   auto kbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? k_lds1 : k_lds0); };
   auto vbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? v_lds1 : v_lds0); };
 
+  // The grid covers the longest sequence; blocks past a shorter one's last tile leave at once.
   const int bh_count = p.B * p.Hq;
   const int id = blockIdx.x;
   const int bh = id % bh_count;
-  const int qt = CAUSAL ? (p.n_qtiles - 1 - id / bh_count) : id / bh_count;
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
+  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  const int Nq = sr.nq, Nk = sr.nk;
+  const int n_qt = (Nq + C::kBR - 1) / C::kBR;
+  if (id / bh_count >= n_qt) return;
+  const int qt = CAUSAL ? (n_qt - 1 - id / bh_count) : id / bh_count;
 
   const int lane = lane_id(), w = wave_id();
   const int h = lane >> 5, col = lane & 31;
   const int q0 = qt * C::kBR;
   const int qw = q0 + 32 * w;
   const int qrow = qw + col;
-  const int diag = p.Nk - p.Nq;
+  const int diag = Nk - Nq;
 
-  const size_t q_slab = (size_t)bh * p.Nq * D;
-  const size_t kv_slab = ((size_t)b * p.Hkv + hkv) * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(p.lse2 + (size_t)bh * p.Nq, (uint32_t)p.Nq * 4);
-  const __amdgpu_buffer_rsrc_t rsd = make_rsrc(p.dsum + (size_t)bh * p.Nq, (uint32_t)p.Nq * 4);
+  const size_t q_row0 = (size_t)p.Hq * sr.tq + (size_t)hq * Nq;     // first row of this (sequence, head)
+  const size_t kv_row0 = (size_t)p.Hkv * sr.tk + (size_t)hkv * Nk;
+  const size_t q_slab = q_row0 * D;
+  const size_t kv_slab = kv_row0 * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const char*)p.dout + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(p.lse2 + q_row0, (uint32_t)Nq * 4);
+  const __amdgpu_buffer_rsrc_t rsd = make_rsrc(p.dsum + q_row0, (uint32_t)Nq * 4);
 
-  int n_tiles = (p.Nk + C::kBC - 1) / C::kBC;
+  int n_tiles = (Nk + C::kBC - 1) / C::kBC;
   if (CAUSAL) {
-    const int last_key = min(q0 + C::kBR, p.Nq) - 1 + diag;
+    const int last_key = min(q0 + C::kBR, Nq) - 1 + diag;
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
 
@@ -810,8 +835,8 @@ void bwd_dq_kernel(DqParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r++) sv[mt][r] = fast_exp2(fmaf(sv[mt][r], p.c, -l2));
     // Only tiles cut by Nk or by the causal diagonal mask P (a uniform branch).
-    if ((k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
-      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
+    if ((k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
+      const int horizon = CAUSAL ? min(qrow + diag, Nk - 1) : Nk - 1;
 #pragma unroll
       for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
@@ -864,7 +889,7 @@ void bwd_dq_kernel(DqParams p) {
     }
   }
 
-  const __amdgpu_buffer_rsrc_t wq = make_rsrc((char*)p.dq + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t wq = make_rsrc((char*)p.dq + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++)
 #pragma unroll
@@ -879,9 +904,13 @@ void bwd_dq_kernel(DqParams p) {
 // Launch
 // ---------------------------------------------------------------------------
 // Phase launchers.  The workspace holds D (rows floats) then lse2 (rows floats).
+// Query rows of the batch (of every head): dense B*Hq*Nq, packed Hq*tot_q.
+int64_t query_rows(const BwdArgs& a) { return a.cu_q ? (int64_t)a.Hq * a.tot_q : (int64_t)a.B * a.Hq * a.Nq; }
+
 template <typename T, int D>
 hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t rows = query_rows(a);
+  if (rows == 0) return hipSuccess;
   constexpr int kTPR = D / (16 / (int)sizeof(T));
   const int64_t threads = rows * kTPR;
   const unsigned grid = (unsigned)((threads + 255) / 256);
@@ -893,14 +922,16 @@ hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   using C = DkvCfg<T, D>;
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t rows = query_rows(a);
   DkvParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = a.dsum + rows; p.dsum = a.dsum;
   p.dk = a.dk; p.dv = a.dv;
+  p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-  p.n_ktiles = (a.Nk + C::kBKV - 1) / C::kBKV;
+  p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.c = a.scale * kLog2e; p.scale = a.scale;
-  const unsigned grid = (unsigned)p.n_ktiles * a.B * a.Hkv;
+  const unsigned grid = (unsigned)((a.Nk + C::kBKV - 1) / C::kBKV) * a.B * a.Hkv;
+  if (grid == 0) return hipSuccess;  // a packed batch with no key
   // 16-bit types take the pipelined kernel; float32 (whose fragments leave
   // no registers for a pipeline) the plain one.
   if constexpr (Elem<T>::kBytes == 2)
@@ -913,13 +944,15 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   using C = DqCfg<T, D>;
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t rows = query_rows(a);
   DqParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = a.dsum + rows; p.dsum = a.dsum; p.dq = a.dq;
+  p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-  p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
+  p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.c = a.scale * kLog2e; p.scale = a.scale;
-  const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
+  const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
+  if (grid == 0) return hipSuccess;  // a packed batch with no query
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -138,6 +138,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kBufferFlags);
 }
 
+// --------------------------------------------------------------------------
+// Sequences of a batch.  Head h of sequence b is one contiguous [n, d] slab
+// that starts at row H * t + h * n of its tensor, where t is the sequence's
+// first token and n its length (H = Hq for Q/O/dO/dQ/LSE, Hkv for K/V/dK/dV).
+// A dense batch has t = b * N and n = N; a packed batch (cu_q != nullptr)
+// takes t and n from the cumulative lengths cu_q / cu_k ([B + 1] int32), and
+// N then bounds every length.  A sequence whose bounds are not
+// 0 <= cu[b] <= cu[b + 1] <= total with a length <= N is read as empty, so a
+// malformed array can never send a slab outside its tensor.
+// --------------------------------------------------------------------------
+struct SeqRows {
+  int nq, nk;  // query and key counts of the sequence
+  int tq, tk;  // first query and first key token of the sequence
+};
+
+__device__ __forceinline__ SeqRows seq_rows(const int* cu_q, const int* cu_k, int b, int Nq, int Nk, int tot_q,
+                                            int tot_k) {
+  if (cu_q == nullptr) return SeqRows{Nq, Nk, b * Nq, b * Nk};
+  const int a0 = cu_q[b], a1 = cu_q[b + 1], c0 = cu_k[b], c1 = cu_k[b + 1];
+  const bool ok = 0 <= a0 && a0 <= a1 && a1 <= tot_q && a1 - a0 <= Nq && 0 <= c0 && c0 <= c1 && c1 <= tot_k &&
+                  c1 - c0 <= Nk;
+  return ok ? SeqRows{a1 - a0, c1 - c0, a0, c0} : SeqRows{0, 0, 0, 0};
+}
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

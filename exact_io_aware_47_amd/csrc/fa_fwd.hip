@@ -73,8 +73,10 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, Nq, Nk;
-  int n_qtiles;
+  const int* cu_q;  // packed batch: cumulative query / key counts [B + 1], else null
+  const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk;  // Nq, Nk: the lengths (dense) or their bounds (packed)
+  int tot_q, tot_k;        // packed batch: total query / key tokens
   float c;  // scale * log2(e)
 };
 
@@ -100,30 +102,37 @@ void fwd_kernel(FwdParams p) {
   auto vbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? v_lds1 : v_lds0); };
 
   // Block -> (query tile, batch, head).  With the causal mask the last query
-  // tiles carry the most work, so they are dispatched first.
+  // tiles carry the most work, so they are dispatched first.  The grid covers
+  // the longest sequence; blocks past a shorter one's last tile leave at once.
   const int bh_count = p.B * p.Hq;
   const int id = blockIdx.x;
   const int bh = id % bh_count;
-  const int qt = CAUSAL ? (p.n_qtiles - 1 - id / bh_count) : id / bh_count;
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
+  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  const int Nq = sr.nq, Nk = sr.nk;
+  const int n_qt = (Nq + C::kBR - 1) / C::kBR;
+  if (id / bh_count >= n_qt) return;
+  const int qt = CAUSAL ? (n_qt - 1 - id / bh_count) : id / bh_count;
 
   const int lane = lane_id(), w = wave_id();
   const int h = lane >> 5, col = lane & 31;
   const int q0 = qt * C::kBR;
   const int qw = q0 + 32 * w;     // first query row of this wave
   const int qrow = qw + col;      // this lane's query row
-  const int diag = p.Nk - p.Nq;   // key j is visible to row i iff j <= i + diag (causal)
+  const int diag = Nk - Nq;       // key j is visible to row i iff j <= i + diag (causal)
 
-  const size_t q_slab = (size_t)bh * p.Nq * D;
-  const size_t kv_slab = ((size_t)b * p.Hkv + hkv) * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)p.Nk * C::kRowBytes);
+  const size_t q_row0 = (size_t)p.Hq * sr.tq + (size_t)hq * Nq;     // first row of this (sequence, head)
+  const size_t kv_row0 = (size_t)p.Hkv * sr.tk + (size_t)hkv * Nk;
+  const size_t q_slab = q_row0 * D;
+  const size_t kv_slab = kv_row0 * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * C::kES, (uint32_t)Nk * C::kRowBytes);
 
-  int n_tiles = (p.Nk + C::kBC - 1) / C::kBC;
+  int n_tiles = (Nk + C::kBC - 1) / C::kBC;
   if (CAUSAL) {
-    const int last_key = min(q0 + C::kBR, p.Nq) - 1 + diag;
+    const int last_key = min(q0 + C::kBR, Nq) - 1 + diag;
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
   auto dma_k = [&](int j, lds_char* dst) __attribute__((always_inline)) {
@@ -256,8 +265,8 @@ void fwd_kernel(FwdParams p) {
     const int k0 = j * C::kBC;
     // Invisible keys (past Nk, past the causal horizon) get score -inf; the
     // rest of the softmax is one code path for every tile.
-    if ((k0 + C::kBC > p.Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
-      const int horizon = CAUSAL ? min(qrow + diag, p.Nk - 1) : p.Nk - 1;
+    if ((k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
+      const int horizon = CAUSAL ? min(qrow + diag, Nk - 1) : Nk - 1;
 #pragma unroll
       for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
@@ -369,7 +378,7 @@ void fwd_kernel(FwdParams p) {
   // ---- epilogue: O = Oᵀ / l, LSE = m + log2(l) in natural log.
   const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + q_slab * C::kES, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
 #pragma unroll
   for (int dt = 0; dt < C::kDT; dt++)
 #pragma unroll
@@ -379,7 +388,7 @@ void fwd_kernel(FwdParams p) {
                 o[dt][4 * a4 + 2] * inv, o[dt][4 * a4 + 3] * inv);
     }
   if (h == 0) {
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)bh * p.Nq, (uint32_t)p.Nq * 4);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + q_row0, (uint32_t)Nq * 4);
     const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
     buf_store4(rl, (uint32_t)qrow * 4, __builtin_bit_cast(uint32_t, lse));
   }
@@ -390,10 +399,12 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<T, D>;
   FwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
+  p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-  p.n_qtiles = (a.Nq + C::kBR - 1) / C::kBR;
+  p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.c = a.scale * kLog2e;
-  const unsigned grid = (unsigned)p.n_qtiles * a.B * a.Hq;
+  const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
+  if (grid == 0) return hipSuccess;  // a packed batch with no query
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);
   return hipGetLastError();
 }

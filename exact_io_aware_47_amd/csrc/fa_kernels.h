@@ -16,6 +16,11 @@ struct FwdArgs {
   float scale;
   bool causal;
   int dtype;  // enum fa_dtype
+  // Packed batch: cumulative query / key counts [B + 1] (device), token
+  // totals; Nq and Nk then bound the sequence lengths.  Null for dense.
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int tot_q = 0, tot_k = 0;
 };
 
 struct BwdArgs {
@@ -28,11 +33,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic [B, Hq, Nq], then LSE_i*log2(e) [B, Hq, Nq]
+  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic (one per query row), then LSE_i*log2(e)
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   bool causal;
   int dtype;
+  const int* cu_q = nullptr;  // packed batch, as in FwdArgs
+  const int* cu_k = nullptr;
+  int tot_q = 0, tot_k = 0;
 };
 
 struct DecodeArgs {

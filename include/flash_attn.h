@@ -142,6 +142,54 @@ int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* d
                       int dtype, const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Packed (variable-length) batches.  Sources: the related-work page
+ * (CuFlash-Attn), repository comparison (variable-length support of the
+ * reference implementation); the concept page "Flash-Attention", key
+ * observation 4 (packing sequences of different lengths); the tutorial's
+ * "Validation checklist" (variable-length sequences).  The pages fix no
+ * layout.  Here a packed batch is the concatenation of each sequence's dense
+ * [1, H, n_b, d] tensor:
+ *   cu_seqlens_q [B + 1] int32 device array: 0 = cu[0] <= cu[1] <= ... <=
+ *                cu[B] = total_q; sequence b has n_b = cu[b+1] - cu[b]
+ *                queries (cu_seqlens_k likewise for keys; n_b may be 0).
+ *   Q, O, dO, dQ [Hq  * total_q, d]: head h of sequence b is the contiguous
+ *                [n_b, d] block starting at row Hq * cu_q[b] + h * n_b.
+ *   K, V, dK, dV [Hkv * total_k, d]: likewise with Hkv and cu_seqlens_k.
+ *   LSE          [Hq  * total_q] float32, the same row order as O.
+ * Each sequence is attended on its own (its queries see only its keys), with
+ * the causal mask aligned bottom-right within the sequence; a sequence with
+ * queries but no keys gives O = 0 and LSE = -inf, one with keys but no
+ * queries gives dK = dV = 0.  max_seqlen_q / max_seqlen_k bound every n_b
+ * (the grids are sized by them) and may not exceed total_q / total_k.
+ * Sizes: B, Hq, Hkv >= 1; total_q, total_k, max_seqlen_q, max_seqlen_k >= 0;
+ * Hq*total_q*d and Hkv*total_k*d below 2^31 elements.
+ * The cumulative arrays live on the device, so the host cannot check them:
+ * a sequence whose entries break the ordering above or exceed the bounds is
+ * skipped (its output rows are left unwritten) and no access leaves the
+ * tensors.  Errors: as the dense calls, with the packed sizes.
+ */
+int flash_attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                          int d, float scale, int causal, int dtype, void* stream);
+
+/* Bytes of device workspace flash_attn_bwd_varlen needs: two float32 values
+ * per query row (Hq * total_q rows).  Returns 0 for invalid sizes (and for
+ * total_q = 0, when no workspace is needed and NULL is accepted). */
+size_t flash_attn_bwd_varlen_workspace_bytes(int B, int Hq, int Hkv, int total_q, int total_k,
+                                             int max_seqlen_q, int max_seqlen_k, int d, int dtype);
+
+/* Backward of flash_attn_fwd_varlen: dQ, dK, dV (fully overwritten) from Q,
+ * K, V, O, LSE and dO, all in the packed layout above.  Deterministic, like
+ * flash_attn_bwd, whose errors (and order) it shares. */
+int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, void* dQ, void* dK, void* dV,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                          int d, float scale, int causal, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Number of KV splits the decode uses for num_splits = 0 (automatic): enough
  * work-groups to cover the 256 compute units several times over, with at
  * least 4 pages per split.  Pure host arithmetic, no HIP call.

@@ -17,10 +17,15 @@ configurations; the pages themselves publish no inputs or seeds):
   reached through a seeded random permutation block table.
 * ``gqa_bf16_4k``     B=2 Hq=32 Hkv=8 N=4096 d=128 bf16, causal (grouped-query
   training shape; not one of the five configurations)
+* ``varlen_bf16``     a packed batch of 16 causal sequences (Hq=Hkv=16,
+  d=128, bf16) whose lengths are drawn uniformly from [1, 4096] by the seeded
+  generator (not one of the five configurations; the pages name packed
+  variable-length batches but give no length mix)
 
 Draw order for a forward/backward workload: Q, K, V, dO, each i.i.d. N(0, 1)
 from ``torch.Generator('cpu').manual_seed(seed)``.  For decode: Q, K cache,
-V cache, then the page permutation.
+V cache, then the page permutation.  For a packed batch: the sequence lengths
+(when drawn), then Q, K, V, dO.
 """
 
 from __future__ import annotations
@@ -37,6 +42,8 @@ __all__ = [
     "DTYPES",
     "make_attention_inputs",
     "make_decode_inputs",
+    "make_packed_inputs",
+    "PackedWorkload",
 ]
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -87,6 +94,23 @@ class DecodeWorkload:
         return self.B * self.max_blocks + self.extra_blocks
 
 
+@dataclass(frozen=True)
+class PackedWorkload:
+    name: str
+    B: int            # sequences in the batch
+    Hq: int
+    Hkv: int
+    max_len: int      # lengths drawn uniformly from [1, max_len]
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
 WORKLOADS = {
     "mha_f32_small": AttnWorkload("mha_f32_small", 1, 1, 1, 128, 128, 32, "f32", (False,), 47001),
     "mha_f16": AttnWorkload("mha_f16", 4, 8, 8, 1024, 1024, 64, "f16", (True, False), 47002),
@@ -96,6 +120,8 @@ WORKLOADS = {
     "decode_gqa_paged": DecodeWorkload("decode_gqa_paged", 8, 32, 8, 32768, 128, "bf16", 47005),
     # grouped-query training shape: four query heads per K/V head
     "gqa_bf16_4k": AttnWorkload("gqa_bf16_4k", 2, 32, 8, 4096, 4096, 128, "bf16", (True,), 47006),
+    # packed batch of variable-length causal sequences
+    "varlen_bf16": PackedWorkload("varlen_bf16", 16, 16, 16, 4096, 128, "bf16", True, 47007),
 }
 
 
@@ -145,6 +171,38 @@ def make_decode_inputs(B, Hq, Hkv, seq_lens, d, dtype: str, seed: int, block_siz
     perm = torch.randperm(num_blocks, generator=gen)
     block_table = perm[: B * max_blocks].view(B, max_blocks).to(torch.int32).contiguous()
     return q, k_cache, v_cache, block_table, seq_lens
+
+
+def make_packed_inputs(lens_q, lens_k, Hq, Hkv, d, dtype: str, seed: int, max_len: int = 0):
+    """Inputs of a packed (variable-length) batch.
+
+    ``lens_q`` / ``lens_k`` list the query / key count of each sequence; with
+    ``lens_q=None`` and ``max_len > 0``, ``lens_k`` must be the number of
+    sequences and equal query and key lengths are drawn uniformly from
+    [1, max_len] (first, from the same generator).  Returns
+    (q [Hq*total_q, d], k, v [Hkv*total_k, d], dO like q, cu_q, cu_k [B+1]
+    int32), where head h of sequence b occupies rows H*cu[b] + h*n_b, ...
+    (each sequence's dense [H, n_b, d] block, concatenated).
+    """
+    tdt = DTYPES[dtype]
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    if lens_q is None:
+        lens_q = torch.randint(1, max_len + 1, (int(lens_k),), generator=gen).tolist()
+        lens_k = list(lens_q)
+    if len(lens_q) != len(lens_k):
+        raise ValueError("lens_q and lens_k must have one entry per sequence")
+    cu_q = torch.tensor([0] + list(lens_q), dtype=torch.int64).cumsum(0).to(torch.int32)
+    cu_k = torch.tensor([0] + list(lens_k), dtype=torch.int64).cumsum(0).to(torch.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = _normal(gen, (Hq * tq, d)).to(tdt)
+    k = _normal(gen, (Hkv * tk, d)).to(tdt)
+    v = _normal(gen, (Hkv * tk, d)).to(tdt)
+    do = _normal(gen, (Hq * tq, d)).to(tdt)
+    return q, k, v, do, cu_q, cu_k
+
+
+def workload_packed_inputs(w: PackedWorkload):
+    return make_packed_inputs(None, w.B, w.Hq, w.Hkv, w.d, w.dtype, w.seed, max_len=w.max_len)
 
 
 def workload_attention_inputs(w: AttnWorkload):

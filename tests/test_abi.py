@@ -50,7 +50,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_decode_paged", "flash_attn_strerror",
-              "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits"):
+              "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits",
+              "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes"):
         assert n in names
 
 
@@ -105,6 +106,48 @@ def test_bwd_validation(L, kw, code):
     assert bwd(L, **kw) == code
 
 
+def fwd_vl(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=3, Hq=4, Hkv=2, tq=300, tk=300, mq=200, mk=200, d=128,
+           scale=0.1, causal=1, dtype=BF16):
+    return L.flash_attn_fwd_varlen(q, k, v, o, lse, cq, ck, B, Hq, Hkv, tq, tk, mq, mk, d, scale, causal, dtype, None)
+
+
+VARLEN_CASES = [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(cq=None), NULL), (dict(ck=None), NULL),
+    (dict(dtype=3), DTYPE),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(tq=-1), SHAPE), (dict(tk=-1), SHAPE), (dict(mq=-1), SHAPE),
+    (dict(mq=301), SHAPE), (dict(mk=301), SHAPE),
+    (dict(d=80), HEADDIM), (dict(Hq=6, Hkv=4), GQA),
+    (dict(tq=1 << 22, mq=10), SHAPE), (dict(Hkv=4, tk=1 << 22, mk=10), SHAPE),
+    (dict(B=1 << 28, tq=100, mq=100), SHAPE),
+    (dict(scale=NAN), SCALE),
+    (dict(), ALIGN), (dict(tq=0, mq=0, tk=0, mk=0), ALIGN), (dict(dtype=F32, causal=0), ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,code", VARLEN_CASES)
+def test_fwd_varlen_validation(L, kw, code):
+    assert fwd_vl(L, **kw) == code
+
+
+def bwd_vl(L, ws=P, ws_bytes=1 << 20, B=3, Hq=4, Hkv=2, tq=300, tk=300, mq=200, mk=200, d=64, scale=0.1,
+           dtype=F16, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(11)]
+    return L.flash_attn_bwd_varlen(*ptrs, B, Hq, Hkv, tq, tk, mq, mk, d, scale, 1, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nulls=(0,)), NULL), (dict(nulls=(5,)), NULL), (dict(nulls=(8,)), NULL), (dict(nulls=(9,)), NULL),
+    (dict(nulls=(10,)), NULL), (dict(dtype=9), DTYPE), (dict(mk=301), SHAPE), (dict(d=48), HEADDIM),
+    (dict(Hq=3, Hkv=2), GQA), (dict(scale=INF), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=2 * 4 * 300 * 4 - 1), WORKSPACE),
+    (dict(ws_bytes=2 * 4 * 300 * 4), ALIGN),
+    # no query rows: no workspace is needed, so NULL is accepted
+    (dict(ws=None, ws_bytes=0, tq=0, mq=0), ALIGN),
+])
+def test_bwd_varlen_validation(L, kw, code):
+    assert bwd_vl(L, **kw) == code
+
+
 def dec(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, bs=16, max_blocks=4,
         nblocks=8, scale=0.1, splits=0, dtype=BF16, ws=P, ws_bytes=1 << 20):
     return L.flash_attn_decode_paged(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, d, bs, max_blocks, nblocks, scale,
@@ -127,6 +170,9 @@ def test_decode_validation(L, kw, code):
 def test_workspace_queries(L):
     assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 128, BF16) == 2 * 2 * 16 * 4096 * 4
     assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 96, BF16) == 0
+    assert L.flash_attn_bwd_varlen_workspace_bytes(16, 16, 16, 35457, 35457, 4000, 4000, 128, BF16) == 2 * 16 * 35457 * 4
+    assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 0, 10, 0, 10, 64, F16) == 0
+    assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 10, 10, 11, 10, 64, F16) == 0
     # Automatic split count: about 4 work-groups per compute unit, at least 4 pages per split.
     assert L.flash_attn_decode_num_splits(8, 8, 2048, 16) == 16
     assert L.flash_attn_decode_num_splits(1, 1, 2, 16) == 1
