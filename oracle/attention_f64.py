@@ -38,6 +38,11 @@ design notes):
 * a packed (variable-length) batch stores sequence b's rows of every head as
   one [H, n_b, d] block starting at row H * cu[b]; each sequence is attended
   on its own.
+* Paged prefill: the concept page's key observation 4 and the tutorial's
+  "Variant family" section (PagedAttention fused with the tiled kernel).  A
+  chunk of Nq new queries per sequence attends to that sequence's cached
+  tokens; the queries are the sequence's last Nq positions, so the causal
+  mask is the same bottom-right alignment as the dense definition.
 * Packed batches: the related-work page's repository comparison (varlen
   support in the reference implementation), the concept page's key
   observation 4 (variable-length packing) and the tutorial's validation
@@ -61,6 +66,7 @@ __all__ = [
     "attention_fwd",
     "attention_bwd",
     "decode_paged",
+    "prefill_paged",
     "attention_fwd_packed",
     "attention_bwd_packed",
     "gather_pages",
@@ -254,6 +260,29 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
             p, lse_row = attention_probs(q[b, h][None, :], kb[h // g], scale, False)
             o[b, h] = (p @ vb[h // g])[0]
             lse[b, h] = lse_row[0]
+    return o, lse
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float, causal: bool):
+    """Attention of a chunk of queries over a paged KV cache.
+
+    q: [B, Hq, Nq, d], the last Nq positions of each sequence;
+    k_cache, v_cache: [num_blocks, Hkv, block_size, d]; block_table:
+    [B, max_blocks]; seq_lens: [B] cached tokens per sequence (the chunk's
+    own tokens included).  Each sequence's keys are gathered back into a
+    contiguous [Hkv, seq_len, d] block and the dense definition applies,
+    with the bottom-right causal alignment (query i of the chunk sees key j
+    iff j <= i + seq_len - Nq).  Returns O [B, Hq, Nq, d], LSE [B, Hq, Nq].
+    """
+    q = _f64(q)
+    bsz, hq, nq, d = q.shape
+    o = np.zeros((bsz, hq, nq, d))
+    lse = np.zeros((bsz, hq, nq))
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        kb = gather_pages(k_cache, block_table[b], n)[None]
+        vb = gather_pages(v_cache, block_table[b], n)[None]
+        o[b], lse[b] = (x[0] for x in attention_fwd(q[b][None], kb, vb, scale, causal))
     return o, lse
 
 

@@ -350,6 +350,61 @@ def pin_decode_empty_sequence(orc):
     assert (o[0] == 0).all() and np.isneginf(lse[0]).all() and np.isfinite(lse[1]).all()
 
 
+def _scatter_to_pages(rng, k, bs, extra=2):
+    """Independent paging of a contiguous [B, Hkv, n, d] tensor: a random table
+    and a cache whose page table[b, t // bs], slot t % bs holds token t."""
+    b, hkv, n, d = k.shape
+    max_blocks = -(-n // bs)
+    nblk = b * max_blocks + extra
+    table = rng.permutation(nblk)[: b * max_blocks].reshape(b, max_blocks)
+    cache = _rand(rng, nblk, hkv, bs, d)  # unused slots hold noise
+    for bi in range(b):
+        for t in range(n):
+            cache[table[bi, t // bs], :, t % bs] = k[bi, :, t]
+    return cache, table
+
+
+def pin_prefill_paged_equals_contiguous(orc):
+    """A chunk of queries over pages equals the dense definition over the same
+    keys stored contiguously, masked bottom-right (queries are the last
+    positions); sequences shorter than the cache rows ignore the rest."""
+    rng = _rng(18)
+    bs, hq, hkv, d = 4, 4, 2, 3
+    for nq, n, causal in ((5, 13, True), (5, 13, False), (1, 9, True), (6, 6, True), (7, 3, True)):
+        k, v = _rand(rng, 2, hkv, n, d), _rand(rng, 2, hkv, n, d)
+        q = _rand(rng, 2, hq, nq, d)
+        kc, table = _scatter_to_pages(rng, k, bs)
+        vc = np.zeros_like(kc)
+        for bi in range(2):
+            for t in range(n):
+                vc[table[bi, t // bs], :, t % bs] = v[bi, :, t]
+        o, lse = orc.prefill_paged(q, kc, vc, table, [n, n], 0.55, causal)
+        o_ref, lse_ref = orc.attention_fwd(q, k, v, 0.55, causal)
+        assert np.array_equal(np.isinf(lse), np.isinf(lse_ref))
+        assert np.abs(o - o_ref).max() < 1e-14
+        fin = np.isfinite(lse_ref)
+        assert np.abs(lse[fin] - lse_ref[fin]).max() < 1e-14
+        if causal and nq <= n:
+            # the chunk's last query sees every key, its first sees n - nq + 1
+            p_last, _ = orc.attention_probs(q[0, 0], k[0, 0], 0.55, False)
+            assert np.abs(o[0, 0, -1] - (p_last @ v[0, 0])[-1]).max() < 1e-14
+        # a shorter second sequence reads only its own first tokens
+        o2, _ = orc.prefill_paged(q, kc, vc, table, [n, n - 1], 0.55, causal)
+        o2_ref, _ = orc.attention_fwd(q[1:], k[1:, :, : n - 1], v[1:, :, : n - 1], 0.55, causal)
+        assert np.abs(o2[1] - o2_ref[0]).max() < 1e-14 and np.array_equal(o2[0], o[0])
+
+
+def pin_prefill_one_query_is_decode(orc):
+    """With one query per sequence, prefill over pages is the paged decode
+    (the single query is the last position, so the causal mask hides nothing)."""
+    rng = _rng(19)
+    q, kc, vc, table, lens = _paged_case(rng, 3, 4, 2, [13, 1, 8], 5, 4)
+    o_d, lse_d = orc.decode_paged(q, kc, vc, table, lens, 0.45)
+    for causal in (False, True):
+        o, lse = orc.prefill_paged(q[:, :, None, :], kc, vc, table, lens, 0.45, causal)
+        assert np.array_equal(o[:, :, 0], o_d) and np.array_equal(lse[:, :, 0], lse_d)
+
+
 # ---------------------------------------------------------------------------
 # Large logits (max-stability checklist item)
 # ---------------------------------------------------------------------------
@@ -424,6 +479,8 @@ def pin_packed_mixed_lengths(orc):
 
 
 ALL_PINS = [
+    pin_prefill_paged_equals_contiguous,
+    pin_prefill_one_query_is_decode,
     pin_packed_equal_lengths_equals_dense,
     pin_packed_mixed_lengths,
     pin_worked_example_streaming,

@@ -50,6 +50,10 @@ MUTANTS = [
     ("streaming sum not rescaled", "l = l * rescale + float", "l = l + float"),
     ("streaming block sum at old max", "float(np.exp(blk - m_new).sum())", "float(np.exp(blk - max(m, float(blk.max()) - 1.0) + 0 * m_new).sum())"),
     ("merge weights swapped", "return mx, l_a * wa + l_b * wb", "return mx, l_a * wb + l_b * wa"),
+    ("prefill mask top-left", "o[b], lse[b] = (x[0] for x in attention_fwd(q[b][None], kb, vb, scale, causal))",
+     "o[b], lse[b] = (x[0] for x in attention_fwd(q[b][None], kb[:, :, :nq], vb[:, :, :nq], scale, causal))"),
+    ("prefill reads table of sequence 0", "kb = gather_pages(k_cache, block_table[b], n)[None]",
+     "kb = gather_pages(k_cache, block_table[0], n)[None]"),
     ("packed rows without head factor", "    r0 = h * int(cu[b])\n", "    r0 = int(cu[b])\n"),
     ("packed blocks token-major", "return x[r0:r0 + h * n].reshape(1, h, n, x.shape[-1])",
      "return x[r0:r0 + h * n].reshape(1, n, h, x.shape[-1]).transpose(0, 2, 1, 3)"),
