@@ -197,6 +197,24 @@ def bench_varlen(torch, fa, si, steps, warmup):
     return w, lens, per["fwd"] + per["bwd"], per
 
 
+def bench_prefill(torch, fa, si, steps, warmup):
+    """Chunked prefill over the paged cache: one flash_attn_prefill_paged call per step."""
+    w = si.WORKLOADS["prefill_paged_bf16"]
+    q, kc, vc, table, lens = (t.to("cuda") for t in si.workload_prefill_inputs(w))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        fa.prefill_paged(q, kc, vc, table, lens, causal=w.causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fa.prefill_paged(q, kc, vc, table, lens, causal=w.causal, out=out, lse=lse)
+    t1.record()
+    torch.cuda.synchronize()
+    return w, t0.elapsed_time(t1) / steps
+
+
 def bench_decode(torch, fa, si, steps, warmup):
     w = si.WORKLOADS["decode_gqa_paged"]
     q, kc, vc, table, lens = (t.to("cuda") for t in si.workload_decode_inputs(w))
@@ -435,6 +453,14 @@ def main(argv=None):
                       "fwd_tflops": round(flv["fwd"] / (per_v["fwd"] * 1e-3) / 1e12, 2),
                       "bwd_tflops": round((flv["dkdv"] + flv["dq"]) / (per_v["bwd"] * 1e-3) / 1e12, 2),
                       "ms_per_step": round(ms_v, 4), "us": {n: round(v * 1e3, 2) for n, v in per_v.items()}}
+    # Chunked prefill over the paged cache (queries are each sequence's last Nq positions).
+    wp, ms_p = bench_prefill(torch, fa, si, args.steps, args.warmup)
+    flp = attention_flops(wp.B, wp.Hq, wp.Nq, wp.seq_len, wp.d, wp.causal)["fwd"]
+    line["prefill_paged"] = {"workload": f"prefill_paged_bf16: B={wp.B} Hq={wp.Hq} Hkv={wp.Hkv}, a chunk of {wp.Nq} "
+                                         f"queries over {wp.seq_len} cached tokens, d={wp.d} bf16 causal, "
+                                         "16-token pages via a permuted table",
+                             "us": round(ms_p * 1e3, 2), "TFLOP/s": round(flp / (ms_p * 1e-3) / 1e12, 2),
+                             "flops": flp, "seed": wp.seed}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)

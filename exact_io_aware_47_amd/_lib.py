@@ -42,6 +42,8 @@ SIGNATURES = {
     "flash_attn_bwd_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_prefill_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "flash_attn_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -237,6 +239,31 @@ def bwd_varlen(q, k, v, out, dout, lse, cu_q, cu_k, hq: int, hkv: int, max_seqle
                                        workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "flash_attn_bwd_varlen")
     return dq, dk, dv
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool = True, scale=None, out=None, lse=None):
+    """Attention of a chunk of queries (the last Nq positions of each sequence)
+    over a paged cache.  q [B,Hq,Nq,d]; k_cache, v_cache
+    [num_blocks,Hkv,block_size,d]; block_table [B,max_blocks] int32;
+    seq_lens [B] int32 (cached tokens, the chunk's own included)."""
+    _dense("q", q, ndim=4)
+    _dense("k_cache", k_cache, q.dtype, 4)
+    _dense("v_cache", v_cache, q.dtype, 4)
+    _dense("block_table", block_table, torch.int32, 2)
+    _dense("seq_lens", seq_lens, torch.int32, 1)
+    B, Hq, Nq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape or block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("cache, table or lengths do not match q")
+    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _dense("lse", lse, torch.float32)
+    code = lib().flash_attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                          _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, d, bs, block_table.shape[1], num_blocks,
+                                          _default_scale(d, scale), int(bool(causal)), _dtype_code(q),
+                                          _stream(q.device))
+    _check(code, "flash_attn_prefill_paged")
+    return out, lse
 
 
 def decode_num_splits(B, Hkv, max_blocks_per_seq, block_size=16) -> int:

@@ -205,6 +205,31 @@ int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const voi
   return launch_status(fa::launch_bwd(a, fa::kBwdAll, (hipStream_t)stream));
 }
 
+int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                             const int* seq_lens, void* O, float* LSE, int B, int Hq, int Hkv, int Nq, int d,
+                             int block_size, int max_blocks_per_seq, int num_blocks, float scale, int causal, int dtype,
+                             void* stream) {
+  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !O || !LSE) return FA_ERR_NULL;
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return FA_ERR_SHAPE;
+  if (!headdim_ok(d)) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if (block_size != 16) return FA_ERR_BLOCKSIZE;
+  if ((int64_t)B * Hq * Nq * d >= kMaxElems || (int64_t)Nq * d * elem_bytes(dtype) >= kMaxElems ||
+      (int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)max_blocks_per_seq * block_size >= kMaxElems)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(O, 16) || !aligned(LSE, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = Q; a.k = K_cache; a.v = V_cache; a.o = O; a.lse = LSE;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = max_blocks_per_seq * block_size; a.d = d;
+  a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks;
+  return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {
   if (B <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || block_size != 16) return 0;
   // Aim for 4 work-groups per compute unit, with at least 4 pages per split.

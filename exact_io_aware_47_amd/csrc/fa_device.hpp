@@ -238,21 +238,38 @@ struct Tile {
 // each of the WAVES waves moves an equal share.  Physical slot s holds logical
 // chunk (s % chunks) ^ key(row) of row s / chunks; rows past the resource's
 // range read as zero.
+// PAGED: the tile's rows come from 16-row pages.  The rows one wave moves
+// always lie in a single page (see dma_wave_row0), so r is that wave's page
+// (its first row at byte 0) and tile row i sits at in-page row i % 16.
 template <int ROW_BYTES, int ROWS, int WAVES>
+struct DmaShape {
+  static constexpr int kSlices = ROWS * ROW_BYTES / 1024;
+  // With fewer slices than waves, the first kSlices waves move one each.
+  static constexpr int kPer = kSlices >= WAVES ? kSlices / WAVES : 1;
+  static constexpr int kActive = kSlices >= WAVES ? WAVES : kSlices;
+  static constexpr int kWaveRows = kPer * 1024 / ROW_BYTES;  // rows moved by one wave
+  static_assert(kSlices * 1024 == ROWS * ROW_BYTES && kPer * kActive == kSlices, "tile must split into whole wave slices");
+};
+
+// First tile row moved by wave w (waves at or past kActive move nothing).
+template <int ROW_BYTES, int ROWS, int WAVES>
+__device__ __forceinline__ int dma_wave_row0(int w) {
+  return w * DmaShape<ROW_BYTES, ROWS, WAVES>::kWaveRows;
+}
+
+template <int ROW_BYTES, int ROWS, int WAVES, bool PAGED = false>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, uint32_t g0, lds_char* tile, int w, int lane) {
   using TT = Tile<ROW_BYTES>;
-  constexpr int kSlices = ROWS * ROW_BYTES / 1024;
-  // With fewer slices than waves, the first kSlices waves move one each.
-  constexpr int kPer = kSlices >= WAVES ? kSlices / WAVES : 1;
-  constexpr int kActive = kSlices >= WAVES ? WAVES : kSlices;
-  static_assert(kSlices * 1024 == ROWS * ROW_BYTES && kPer * kActive == kSlices, "tile must split into whole wave slices");
-  if (kActive < WAVES && w >= kActive) return;
+  using S = DmaShape<ROW_BYTES, ROWS, WAVES>;
+  static_assert(!PAGED || (S::kWaveRows <= 16 && 16 % S::kWaveRows == 0 && ROWS % 16 == 0),
+                "a wave's rows must stay within one 16-row page");
+  if (S::kActive < WAVES && w >= S::kActive) return;
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int s0 = (w * kPer + i) * 64;
+  for (int i = 0; i < S::kPer; i++) {
+    const int s0 = (w * S::kPer + i) * 64;
     const int s = s0 + lane;
     const int row = s / TT::kChunks, pc = s % TT::kChunks;
-    buf_load16_to_lds(r, g0 + row * ROW_BYTES + ((pc ^ TT::key(row)) << 4), tile + s0 * 16);
+    buf_load16_to_lds(r, g0 + (PAGED ? (row & 15) : row) * ROW_BYTES + ((pc ^ TT::key(row)) << 4), tile + s0 * 16);
   }
 }
 

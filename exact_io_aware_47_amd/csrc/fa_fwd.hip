@@ -77,15 +77,21 @@ struct FwdParams {
   const int* cu_k;
   int B, Hq, Hkv, Nq, Nk;  // Nq, Nk: the lengths (dense) or their bounds (packed)
   int tot_q, tot_k;        // packed batch: total query / key tokens
+  // Paged KV (k, v are the page caches [num_blocks, Hkv, 16, D]): the block
+  // table [B, max_blocks] and cached tokens per sequence are kernel arguments
+  // of their own (restrict-qualified, read through the scalar cache).
+  int max_blocks, num_blocks;
   float c;  // scale * log2(e)
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
 
 
-template <typename T, int D, bool CAUSAL>
+// PAGED: K and V are read from a paged cache through the block table; the
+// queries are the last Nq positions of each sequence (dense Q, O, LSE).
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_kernel(FwdParams p) {
+void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __restrict__ seq_lens) {
   using C = FwdCfg<T, D>;
   using E = Elem<T>;
   using F = Frags<T>;
@@ -109,7 +115,14 @@ void fwd_kernel(FwdParams p) {
   const int bh = id % bh_count;
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
-  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  SeqRows sr;
+  if constexpr (PAGED) {
+    // Cached tokens of the sequence, clamped to what its table row can address.
+    const int n = min(max(seq_lens[b], 0), p.max_blocks * 16);
+    sr = SeqRows{p.Nq, n, b * p.Nq, 0};
+  } else {
+    sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  }
   const int Nq = sr.nq, Nk = sr.nk;
   const int n_qt = (Nq + C::kBR - 1) / C::kBR;
   if (id / bh_count >= n_qt) return;
@@ -135,13 +148,46 @@ void fwd_kernel(FwdParams p) {
     const int last_key = min(q0 + C::kBR, Nq) - 1 + diag;
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
-  auto dma_k = [&](int j, lds_char* dst) __attribute__((always_inline)) {
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  // Paged KV: the rows a wave moves of any tile lie in one page; PageRef is
+  // that page for one tile (byte offset of its (page, kv head) block in the
+  // cache and bytes of valid rows; 0 bytes reads zeros).
+  struct PageRef {
+    size_t off;
+    uint32_t bytes;
   };
-  auto dma_v = [&](int j, lds_char* dst) __attribute__((always_inline)) {
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  const int wrow0 = dma_wave_row0<C::kRowBytes, C::kBC, C::kWaves>(w);
+  const int* trow = PAGED ? block_table + (size_t)b * p.max_blocks : nullptr;
+  auto page_of = [&](int jj) __attribute__((always_inline)) {
+    PageRef r{0, 0u};
+    if constexpr (PAGED) {
+      const int t0 = jj * C::kBC + wrow0;  // first token of this wave's rows
+      if (jj < n_tiles && t0 < Nk) {
+        const int id = trow[t0 >> 4];
+        if (id >= 0 && id < p.num_blocks) {  // a bad table entry reads as a page of zeros
+          r.off = ((size_t)id * p.Hkv + hkv) * (16 * C::kRowBytes);
+          r.bytes = (uint32_t)min(16, Nk - (t0 & ~15)) * C::kRowBytes;
+        }
+      }
+    }
+    return r;
   };
-  if (n_tiles > 0) dma_k(0, kbuf(0));
+  // Page of tile j (its V is staged one slot pair after its K) and of tile j + 1.
+  PageRef pg_j = page_of(0), pg_j1 = page_of(1);
+  auto dma_k = [&](int j, lds_char* dst, const PageRef& pr) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves, true>(make_rsrc((const char*)p.k + pr.off, pr.bytes), 0u, dst, w,
+                                                      lane);
+    else
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  auto dma_v = [&](int j, lds_char* dst, const PageRef& pr) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves, true>(make_rsrc((const char*)p.v + pr.off, pr.bytes), 0u, dst, w,
+                                                      lane);
+    else
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  if (n_tiles > 0) dma_k(0, kbuf(0), pg_j);
 
   // Qᵀ as the B operand of Sᵀ = K Qᵀ: lane holds row qrow, d = 16ks + 8h + 0..7.
   Frag qf[C::kKS];
@@ -325,8 +371,8 @@ void fwd_kernel(FwdParams p) {
     if constexpr ((p4 & 1) == 0) {
       const int j = t >> 1;
       constexpr int jp = (p4 >> 1) & 1;  // parity of j
-      if (j + 1 < n_tiles) dma_k(j + 1, kbuf(jp ^ 1));
-      if (j < n_tiles) dma_v(j, vbuf(jp));
+      if (j + 1 < n_tiles) dma_k(j + 1, kbuf(jp ^ 1), pg_j1);
+      if (j < n_tiles) dma_v(j, vbuf(jp), pg_j);
     }
     const int u = t - g;
     if (u >= 0) {
@@ -357,6 +403,14 @@ void fwd_kernel(FwdParams p) {
     // (each wave waits for its own) and every wave is done with the buffers
     // that the next even slot refills.  The even slots need no barrier.
     if constexpr (p4 & 1) {
+      if constexpr (PAGED) {
+        // Table entries for the next even slot, read after this slot's LDS
+        // work (the empty asm keeps them there) so that their wait merges
+        // with the barrier's.
+        asm volatile("" ::: "memory");
+        pg_j = pg_j1;
+        pg_j1 = page_of((t >> 1) + 2);
+      }
       wait_vmem();
       barrier_lds();
     }
@@ -394,7 +448,7 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<T, D>;
   FwdParams p;
@@ -402,19 +456,27 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
+  p.max_blocks = a.max_blocks; p.num_blocks = a.num_blocks;
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;  // a packed batch with no query
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, PAGED>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,
+                     a.block_table, a.seq_lens);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
+  if (a.block_table) return a.causal ? launch_typed<T, D, true, true>(a, s) : launch_typed<T, D, false, true>(a, s);
+  return a.causal ? launch_typed<T, D, true, false>(a, s) : launch_typed<T, D, false, false>(a, s);
 }
 
 template <typename T>
 hipError_t launch_dtype(const FwdArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 32: return a.causal ? launch_typed<T, 32, true>(a, s) : launch_typed<T, 32, false>(a, s);
-    case 64: return a.causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
-    case 128: return a.causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+    case 32: return launch_mask<T, 32>(a, s);
+    case 64: return launch_mask<T, 64>(a, s);
+    case 128: return launch_mask<T, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,12 @@ struct FwdArgs {
   const int* cu_q = nullptr;
   const int* cu_k = nullptr;
   int tot_q = 0, tot_k = 0;
+  // Paged KV cache (k, v are [num_blocks, Hkv, 16, d] page caches): block
+  // table [B, max_blocks] and cached tokens per sequence [B] (device).  Null
+  // for contiguous K, V.
+  const int* block_table = nullptr;
+  const int* seq_lens = nullptr;
+  int max_blocks = 0, num_blocks = 0;
 };
 
 struct BwdArgs {

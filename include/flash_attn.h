@@ -236,6 +236,35 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
                             int num_blocks, float scale, int num_splits, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Paged prefill: a chunk of Nq new queries per sequence attends to the
+ * sequence's tokens in a paged KV cache.  Sources: the tutorial's "Variant
+ * family" section (PagedAttention: K/V stored in non-contiguous fixed-size
+ * blocks) and the concept page "Flash-Attention", key observation 4 (paged
+ * KV fused with the tiled kernel).
+ *   Q, O     [B, Hq, Nq, d] dtype: the chunk's queries are the last Nq
+ *            positions of each sequence;
+ *   LSE      [B, Hq, Nq] float32;
+ *   K_cache, V_cache, block_table, seq_lens: as for flash_attn_decode_paged
+ *            (seq_lens[b] counts every cached token of sequence b, the
+ *            chunk's own included; values outside [0, max_blocks_per_seq *
+ *            block_size] are clamped to that range).
+ * causal != 0 applies the bottom-right mask: query i of the chunk sees cached
+ * token j iff j <= i + seq_lens[b] - Nq, so rows with i < Nq - seq_lens[b]
+ * see nothing (O = 0, LSE = -inf).  Without the mask every cached token is
+ * seen.  The tiled forward runs unchanged except that each K/V tile is
+ * staged page by page through the table.  dtype: FA_F32, FA_F16, FA_BF16;
+ * block_size must be 16.  A table entry outside [0, num_blocks) reads as a
+ * page of zeros.
+ * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
+ * FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_LAUNCH.
+ */
+int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_cache,
+                             const int* block_table, const int* seq_lens, void* O, float* LSE,
+                             int B, int Hq, int Hkv, int Nq, int d, int block_size, int max_blocks_per_seq,
+                             int num_blocks, float scale, int causal, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

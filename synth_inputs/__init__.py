@@ -17,6 +17,10 @@ configurations; the pages themselves publish no inputs or seeds):
   reached through a seeded random permutation block table.
 * ``gqa_bf16_4k``     B=2 Hq=32 Hkv=8 N=4096 d=128 bf16, causal (grouped-query
   training shape; not one of the five configurations)
+* ``prefill_paged_bf16`` B=4 Hq=32 Hkv=8 d=128 bf16, causal: a chunk of 1024
+  new queries per sequence over 8192 cached tokens in 16-token pages reached
+  through a seeded random permutation block table (chunked prefill; not one
+  of the five configurations)
 * ``varlen_bf16``     a packed batch of 16 causal sequences (Hq=Hkv=16,
   d=128, bf16) whose lengths are drawn uniformly from [1, 4096] by the seeded
   generator (not one of the five configurations; the pages name packed
@@ -24,7 +28,8 @@ configurations; the pages themselves publish no inputs or seeds):
 
 Draw order for a forward/backward workload: Q, K, V, dO, each i.i.d. N(0, 1)
 from ``torch.Generator('cpu').manual_seed(seed)``.  For decode: Q, K cache,
-V cache, then the page permutation.  For a packed batch: the sequence lengths
+V cache, then the page permutation (paged prefill: the same, with Nq query
+rows per sequence).  For a packed batch: the sequence lengths
 (when drawn), then Q, K, V, dO.
 """
 
@@ -43,6 +48,8 @@ __all__ = [
     "make_attention_inputs",
     "make_decode_inputs",
     "make_packed_inputs",
+    "make_prefill_inputs",
+    "PrefillWorkload",
     "PackedWorkload",
 ]
 
@@ -95,6 +102,25 @@ class DecodeWorkload:
 
 
 @dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int           # new queries per sequence (the chunk)
+    seq_len: int      # cached tokens per sequence, the chunk included
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    block_size: int = 16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclass(frozen=True)
 class PackedWorkload:
     name: str
     B: int            # sequences in the batch
@@ -120,6 +146,8 @@ WORKLOADS = {
     "decode_gqa_paged": DecodeWorkload("decode_gqa_paged", 8, 32, 8, 32768, 128, "bf16", 47005),
     # grouped-query training shape: four query heads per K/V head
     "gqa_bf16_4k": AttnWorkload("gqa_bf16_4k", 2, 32, 8, 4096, 4096, 128, "bf16", (True,), 47006),
+    # chunked prefill over a paged cache
+    "prefill_paged_bf16": PrefillWorkload("prefill_paged_bf16", 4, 32, 8, 1024, 8192, 128, "bf16", True, 47008),
     # packed batch of variable-length causal sequences
     "varlen_bf16": PackedWorkload("varlen_bf16", 16, 16, 16, 4096, 128, "bf16", True, 47007),
 }
@@ -171,6 +199,30 @@ def make_decode_inputs(B, Hq, Hkv, seq_lens, d, dtype: str, seed: int, block_siz
     perm = torch.randperm(num_blocks, generator=gen)
     block_table = perm[: B * max_blocks].view(B, max_blocks).to(torch.int32).contiguous()
     return q, k_cache, v_cache, block_table, seq_lens
+
+
+def make_prefill_inputs(B, Hq, Hkv, Nq, seq_lens, d, dtype: str, seed: int, block_size: int = 16,
+                        extra_blocks: int = 0):
+    """Inputs of a chunked prefill over a paged cache: as make_decode_inputs,
+    but with Nq query rows per sequence (q [B, Hq, Nq, d]).  Draw order: Q,
+    K cache, V cache, page permutation."""
+    tdt = DTYPES[dtype]
+    if isinstance(seq_lens, int):
+        seq_lens = [seq_lens] * B
+    seq_lens = torch.tensor(seq_lens, dtype=torch.int32)
+    max_blocks = max(1, -(-int(seq_lens.max()) // block_size))
+    num_blocks = B * max_blocks + extra_blocks
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = _normal(gen, (B, Hq, Nq, d)).to(tdt)
+    k_cache = _normal(gen, (num_blocks, Hkv, block_size, d)).to(tdt)
+    v_cache = _normal(gen, (num_blocks, Hkv, block_size, d)).to(tdt)
+    perm = torch.randperm(num_blocks, generator=gen)
+    block_table = perm[: B * max_blocks].view(B, max_blocks).to(torch.int32).contiguous()
+    return q, k_cache, v_cache, block_table, seq_lens
+
+
+def workload_prefill_inputs(w: PrefillWorkload):
+    return make_prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.seq_len, w.d, w.dtype, w.seed, w.block_size)
 
 
 def make_packed_inputs(lens_q, lens_k, Hq, Hkv, d, dtype: str, seed: int, max_len: int = 0):

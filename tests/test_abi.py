@@ -51,7 +51,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_decode_paged", "flash_attn_strerror",
               "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits",
-              "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes"):
+              "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes",
+              "flash_attn_prefill_paged"):
         assert n in names
 
 
@@ -165,6 +166,24 @@ def dec(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128
 ])
 def test_decode_validation(L, kw, code):
     assert dec(L, **kw) == code
+
+
+def pre(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=64, d=128, bs=16, max_blocks=8,
+        nblocks=20, scale=0.1, causal=1, dtype=BF16):
+    return L.flash_attn_prefill_paged(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, Nq, d, bs, max_blocks, nblocks, scale,
+                                      causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(vc=None), NULL), (dict(table=None), NULL), (dict(lens=None), NULL),
+    (dict(lse=None), NULL), (dict(dtype=3), DTYPE),
+    (dict(B=0), SHAPE), (dict(Nq=0), SHAPE), (dict(max_blocks=0), SHAPE), (dict(nblocks=0), SHAPE),
+    (dict(d=80), HEADDIM), (dict(Hq=8, Hkv=3), GQA), (dict(bs=32), BLOCKSIZE),
+    (dict(max_blocks=1 << 27), SHAPE), (dict(B=1 << 12, Nq=1 << 12), SHAPE),
+    (dict(scale=NAN), SCALE), (dict(), ALIGN), (dict(dtype=F32, causal=0), ALIGN),
+])
+def test_prefill_validation(L, kw, code):
+    assert pre(L, **kw) == code
 
 
 def test_workspace_queries(L):
