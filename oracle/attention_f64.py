@@ -43,6 +43,13 @@ design notes):
   chunk of Nq new queries per sequence attends to that sequence's cached
   tokens; the queries are the sequence's last Nq positions, so the causal
   mask is the same bottom-right alignment as the dense definition.
+* FP8 forward: the concept page's key observations (FlashAttention-3's FP8
+  path) and the tutorial's validation checklist (FP8).  The pages give no
+  encoding or scaling recipe.  Reading: inputs are OCP FP8 E4M3 codes (sign,
+  4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+  subnormal; S.1111.111 is NaN; no infinities) times one float32 descale
+  factor per tensor.  The oracle decodes the codes from that definition and
+  applies the dense definition to the decoded values.
 * Packed batches: the related-work page's repository comparison (varlen
   support in the reference implementation), the concept page's key
   observation 4 (variable-length packing) and the tutorial's validation
@@ -67,6 +74,8 @@ __all__ = [
     "attention_bwd",
     "decode_paged",
     "prefill_paged",
+    "fp8_e4m3_decode",
+    "attention_fwd_fp8",
     "attention_fwd_packed",
     "attention_bwd_packed",
     "gather_pages",
@@ -173,6 +182,33 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool, row_ids=None, nq_tota
             dk[b, h // g] += scale * (ds.T @ q[b, h])
             dv[b, h // g] += p.T @ do[b, h]
     return dq, dk, dv
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8 array) in float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent e (bias 7), bits 2..0 the
+    mantissa f: e > 0 gives (1 + f/8) * 2^(e-7), e = 0 gives (f/8) * 2^-6,
+    and e = 15 with f = 7 is NaN (the format has no infinities).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    f = (c & 0x7).astype(np.float64)
+    mag = np.where(e > 0, (1.0 + f / 8.0) * np.exp2(e - 7.0), (f / 8.0) * 2.0 ** -6)
+    mag = np.where((e == 15) & (f == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_fwd_fp8(q_codes, k_codes, v_codes, q_descale: float, k_descale: float, v_descale: float,
+                      scale: float, causal: bool):
+    """Forward on FP8 inputs: each tensor is its E4M3 codes times its descale.
+    q_codes [B, Hq, Nq, d], k_codes / v_codes [B, Hkv, Nk, d] (uint8).
+    Returns O [B, Hq, Nq, d], LSE [B, Hq, Nq] of the decoded tensors."""
+    q = fp8_e4m3_decode(q_codes) * q_descale
+    k = fp8_e4m3_decode(k_codes) * k_descale
+    v = fp8_e4m3_decode(v_codes) * v_descale
+    return attention_fwd(q, k, v, scale, causal)
 
 
 def _unpack(x, cu, h: int, b: int):

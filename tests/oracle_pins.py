@@ -405,6 +405,42 @@ def pin_prefill_one_query_is_decode(orc):
         assert np.array_equal(o[:, :, 0], o_d) and np.array_equal(lse[:, :, 0], lse_d)
 
 
+def pin_fp8_decode_definition(orc):
+    """E4M3 values the format fixes, and agreement with torch's float8_e4m3fn
+    on all 256 codes (NaN codes included)."""
+    import torch
+    v = orc.fp8_e4m3_decode(np.array([0x00, 0x80, 0x38, 0xB8, 0x7E, 0xFE, 0x08, 0x07, 0x01, 0x40, 0x3C, 0x7F, 0xFF],
+                                     dtype=np.uint8))
+    exp = [0.0, -0.0, 1.0, -1.0, 448.0, -448.0, 2.0 ** -6, 7 * 2.0 ** -9, 2.0 ** -9, 2.0, 1.5]
+    assert np.array_equal(v[:11], exp) and np.isnan(v[11]) and np.isnan(v[12])
+    assert np.signbit(v[1]) and not np.signbit(v[0])
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = orc.fp8_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(mine[fin], ref[fin])
+    # every finite code is distinct from its neighbours except the two zeros
+    assert len(set(mine[fin].tolist())) == fin.sum() - 1
+
+
+def pin_fp8_attention_descales(orc):
+    """FP8 attention is the dense definition of the decoded tensors: scaling
+    V's descale scales O; Q's or K's descale acts as the softmax scale."""
+    rng = _rng(21)
+    codes = lambda *sh: rng.integers(0, 256, size=sh).astype(np.uint8) & 0xF7  # no NaN codes (S.1111.111)
+    q, k, v = codes(1, 2, 9, 8), codes(1, 1, 11, 8), codes(1, 1, 11, 8)
+    for causal in (False, True):
+        o, lse = orc.attention_fwd_fp8(q, k, v, 0.5, 0.25, 1.0, 0.3, causal)
+        o2, lse2 = orc.attention_fwd_fp8(q, k, v, 0.5, 0.25, 2.0, 0.3, causal)
+        assert np.array_equal(o2, 2.0 * o) and np.array_equal(lse2, lse)
+        o3, lse3 = orc.attention_fwd_fp8(q, k, v, 1.0, 0.25, 1.0, 0.15, causal)
+        assert np.abs(o3 - o).max() < 1e-13 and np.abs(lse3 - lse).max() < 1e-13
+        dq, dk, dv = (orc.fp8_e4m3_decode(x) for x in (q, k, v))
+        o4, lse4 = orc.attention_fwd(dq * 0.5, dk * 0.25, dv, 0.3, causal)
+        assert np.array_equal(o4, o) and np.array_equal(lse4, lse)
+
+
 # ---------------------------------------------------------------------------
 # Large logits (max-stability checklist item)
 # ---------------------------------------------------------------------------
@@ -479,6 +515,8 @@ def pin_packed_mixed_lengths(orc):
 
 
 ALL_PINS = [
+    pin_fp8_decode_definition,
+    pin_fp8_attention_descales,
     pin_prefill_paged_equals_contiguous,
     pin_prefill_one_query_is_decode,
     pin_packed_equal_lengths_equals_dense,

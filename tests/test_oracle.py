@@ -54,6 +54,9 @@ MUTANTS = [
      "o[b], lse[b] = (x[0] for x in attention_fwd(q[b][None], kb[:, :, :nq], vb[:, :, :nq], scale, causal))"),
     ("prefill reads table of sequence 0", "kb = gather_pages(k_cache, block_table[b], n)[None]",
      "kb = gather_pages(k_cache, block_table[0], n)[None]"),
+    ("fp8 exponent bias 8", "(1.0 + f / 8.0) * np.exp2(e - 7.0)", "(1.0 + f / 8.0) * np.exp2(e - 8.0)"),
+    ("fp8 subnormals without the 2^-6 scale", "(f / 8.0) * 2.0 ** -6", "(f / 8.0) * 2.0 ** -7"),
+    ("fp8 V descale dropped", "v = fp8_e4m3_decode(v_codes) * v_descale", "v = fp8_e4m3_decode(v_codes)"),
     ("packed rows without head factor", "    r0 = h * int(cu[b])\n", "    r0 = int(cu[b])\n"),
     ("packed blocks token-major", "return x[r0:r0 + h * n].reshape(1, h, n, x.shape[-1])",
      "return x[r0:r0 + h * n].reshape(1, n, h, x.shape[-1]).transpose(0, 2, 1, 3)"),
