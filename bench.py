@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_BF16 = 2516.6  # TFLOP/s: 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_MFMA_FP8 = 5033.2   # TFLOP/s: dense fp8, twice the bf16 rate
 PEAK_HBM = 8000.0        # GB/s: MI355X HBM3E
 METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4096, d=128, causal) + % of MFMA peak"
 
@@ -210,6 +211,28 @@ def bench_prefill(torch, fa, si, steps, warmup):
     t0.record()
     for _ in range(steps):
         fa.prefill_paged(q, kc, vc, table, lens, causal=w.causal, out=out, lse=lse)
+    t1.record()
+    torch.cuda.synchronize()
+    return w, t0.elapsed_time(t1) / steps
+
+
+def bench_fp8(torch, fa, si, steps, warmup):
+    """FP8 forward on the training shape: one flash_attn_fwd_fp8 call per step
+    (its V-staging pre-pass included)."""
+    w = si.WORKLOADS["mha_fp8_4k"]
+    q, k, v, desc = si.make_fp8_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+    q, k, v = q.to("cuda"), k.to("cuda"), v.to("cuda")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fwd_fp8_workspace_bytes(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device="cuda")
+    call = lambda: fa.fwd_fp8(q, k, v, *desc, causal=True, out=out, lse=lse, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
     t1.record()
     torch.cuda.synchronize()
     return w, t0.elapsed_time(t1) / steps
@@ -461,6 +484,15 @@ def main(argv=None):
                                          "16-token pages via a permuted table",
                              "us": round(ms_p * 1e3, 2), "TFLOP/s": round(flp / (ms_p * 1e-3) / 1e12, 2),
                              "flops": flp, "seed": wp.seed}
+    # FP8 (E4M3) forward on the same shape.
+    wf, ms_f = bench_fp8(torch, fa, si, args.steps, args.warmup)
+    flf = attention_flops(wf.B, wf.Hq, wf.Nq, wf.Nk, wf.d, True)["fwd"]
+    tf = flf / (ms_f * 1e-3) / 1e12
+    line["fp8"] = {"workload": "mha_fp8_4k: causal forward, B=2 H=16 N=4096 d=128, E4M3 Q/K/V with per-tensor "
+                               "descales, bf16 O", "us": round(ms_f * 1e3, 2), "TFLOP/s": round(tf, 2),
+                   "roofline": {"kernel": "fwd_fp8 (V staging + forward)", "bound": "mfma", "achieved": round(tf, 2),
+                                "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_FP8, 4),
+                                "traffic": None}}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)

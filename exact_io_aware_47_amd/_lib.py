@@ -44,6 +44,8 @@ SIGNATURES = {
                                    _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "flash_attn_prefill_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "flash_attn_fwd_fp8_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "flash_attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp, _sz, _vp]),
     "flash_attn_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -263,6 +265,38 @@ def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool = Tru
                                           _default_scale(d, scale), int(bool(causal)), _dtype_code(q),
                                           _stream(q.device))
     _check(code, "flash_attn_prefill_paged")
+    return out, lse
+
+
+def fwd_fp8_workspace_bytes(B, Hkv, Nk, d) -> int:
+    return int(lib().flash_attn_fwd_fp8_workspace_bytes(B, Hkv, Nk, d))
+
+
+def fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal: bool = False, scale=None, out=None,
+            lse=None, workspace=None):
+    """O (bf16), LSE of FP8 inputs: q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d] as
+    torch.float8_e4m3fn (or uint8 codes), each times its descale."""
+    _dense("q", q, ndim=4)
+    for name, t in (("k", k), ("v", v)):
+        _dense(name, t, q.dtype, 4)
+    if q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError(f"fp8 inputs must be torch.float8_e4m3fn or uint8 codes, got {q.dtype}")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else \
+        _dense("out", out, torch.bfloat16)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _dense("lse", lse, torch.float32)
+    ws_bytes = fwd_fp8_workspace_bytes(B, Hkv, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    code = lib().flash_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                    _default_scale(d, scale), float(q_descale), float(k_descale), float(v_descale),
+                                    int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(q.device))
+    _check(code, "flash_attn_fwd_fp8")
     return out, lse
 
 

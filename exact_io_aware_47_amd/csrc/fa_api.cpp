@@ -230,6 +230,38 @@ int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_c
   return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
+size_t flash_attn_fwd_fp8_workspace_bytes(int B, int Hkv, int Nk, int d) {
+  if (B <= 0 || Hkv <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+  return fa::fp8_vt_bytes(B, Hkv, Nk, d);
+}
+
+int flash_attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int d, float scale, float q_descale, float k_descale, float v_descale,
+                       int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  // Element counts and 32-bit byte offsets of the slabs (bf16 O is the widest),
+  // and the pre-pass grid's second dimension.
+  if ((int64_t)B * Hq * Nq * d >= kMaxElems || (int64_t)B * Hkv * (Nk + 63) / 64 * 64 * d >= kMaxElems ||
+      (int64_t)Nq * d * 2 >= kMaxElems || (int64_t)(Nk + 63) / 64 * 64 * d >= kMaxElems || (int64_t)B * Hkv > 65535)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale) ||
+      !isfinite(scale * q_descale * k_descale))
+    return FA_ERR_SCALE;
+  if (!workspace || workspace_bytes < flash_attn_fwd_fp8_workspace_bytes(B, Hkv, Nk, d)) return FA_ERR_WORKSPACE;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4) ||
+      !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  fa::Fp8FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE; a.workspace = workspace;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale; a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
+  a.causal = causal != 0;
+  return launch_status(fa::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {
   if (B <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || block_size != 16) return 0;
   // Aim for 4 work-groups per compute unit, with at least 4 pages per split.

@@ -63,7 +63,23 @@ struct DecodeArgs {
   int dtype;
 };
 
+// FP8 (E4M3) forward: q, k, v are E4M3 codes, o is bf16; workspace holds
+// the staged Vᵀ tiles (fp8_vt_bytes).
+struct Fp8FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale, q_descale, k_descale, v_descale;
+  bool causal;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
+size_t fp8_vt_bytes(int B, int Hkv, int Nk, int d);
 // Backward phases (bit mask); kBwdAll runs them in order on one stream.
 constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);

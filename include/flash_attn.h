@@ -265,6 +265,34 @@ int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_c
                              int B, int Hq, int Hkv, int Nq, int d, int block_size, int max_blocks_per_seq,
                              int num_blocks, float scale, int causal, int dtype, void* stream);
 
+/*
+ * FP8 forward.  Sources: the concept page "Flash-Attention", key
+ * observations (FlashAttention-3's FP8 path on Hopper) and the tutorial's
+ * "Validation checklist" (FP8).  The pages give no encoding or scaling
+ * recipe; here:
+ *   Q [B, Hq, Nq, d], K, V [B, Hkv, Nk, d]: OCP FP8 E4M3 codes (one byte per
+ *   element); the value of an element is its code times the tensor's float32
+ *   descale (q_descale, k_descale, v_descale, all finite).
+ *   O [B, Hq, Nq, d] bfloat16; LSE [B, Hq, Nq] float32 (natural log), as for
+ *   flash_attn_fwd, of the decoded tensors.
+ * Both products run on the FP8 matrix cores with float32 accumulation; the
+ * probabilities are rounded to E4M3 (round to nearest even, after scaling
+ * into (0, 256]) before the second product, while the softmax row sum is
+ * taken in float32 from the unrounded values.  d must be 64 or 128 (else
+ * FA_ERR_HEADDIM).  causal as for flash_attn_fwd.
+ * workspace: flash_attn_fwd_fp8_workspace_bytes(...) bytes of device memory
+ * (V is staged there transposed, 64 keys per tile); contents on entry are
+ * ignored.  B * Hkv must not exceed 65535.
+ * Errors (in this order): FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM,
+ * FA_ERR_GQA, FA_ERR_SHAPE (too large), FA_ERR_SCALE, FA_ERR_WORKSPACE,
+ * FA_ERR_ALIGN, FA_ERR_LAUNCH.
+ */
+size_t flash_attn_fwd_fp8_workspace_bytes(int B, int Hkv, int Nk, int d);
+int flash_attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       float scale, float q_descale, float k_descale, float v_descale, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,9 @@ configurations; the pages themselves publish no inputs or seeds):
   new queries per sequence over 8192 cached tokens in 16-token pages reached
   through a seeded random permutation block table (chunked prefill; not one
   of the five configurations)
+* ``mha_fp8_4k``      B=2 H=16 N=4096 d=128, causal, FP8 E4M3 inputs: the
+  N(0,1) draws of Q, K, V divided by a per-tensor descale amax/448 and
+  rounded to E4M3 (the FP8 forward; not one of the five configurations)
 * ``varlen_bf16``     a packed batch of 16 causal sequences (Hq=Hkv=16,
   d=128, bf16) whose lengths are drawn uniformly from [1, 4096] by the seeded
   generator (not one of the five configurations; the pages name packed
@@ -49,6 +52,7 @@ __all__ = [
     "make_decode_inputs",
     "make_packed_inputs",
     "make_prefill_inputs",
+    "make_fp8_inputs",
     "PrefillWorkload",
     "PackedWorkload",
 ]
@@ -146,6 +150,8 @@ WORKLOADS = {
     "decode_gqa_paged": DecodeWorkload("decode_gqa_paged", 8, 32, 8, 32768, 128, "bf16", 47005),
     # grouped-query training shape: four query heads per K/V head
     "gqa_bf16_4k": AttnWorkload("gqa_bf16_4k", 2, 32, 8, 4096, 4096, 128, "bf16", (True,), 47006),
+    # FP8 forward on the training shape (E4M3 codes with amax/448 descales)
+    "mha_fp8_4k": AttnWorkload("mha_fp8_4k", 2, 16, 16, 4096, 4096, 128, "fp8", (True,), 47009),
     # chunked prefill over a paged cache
     "prefill_paged_bf16": PrefillWorkload("prefill_paged_bf16", 4, 32, 8, 1024, 8192, 128, "bf16", True, 47008),
     # packed batch of variable-length causal sequences
@@ -199,6 +205,22 @@ def make_decode_inputs(B, Hq, Hkv, seq_lens, d, dtype: str, seed: int, block_siz
     perm = torch.randperm(num_blocks, generator=gen)
     block_table = perm[: B * max_blocks].view(B, max_blocks).to(torch.int32).contiguous()
     return q, k_cache, v_cache, block_table, seq_lens
+
+
+def make_fp8_inputs(B, Hq, Hkv, Nq, Nk, d, seed: int):
+    """FP8 inputs: float32 N(0,1) draws of Q, K, V (in that order), each
+    divided by its per-tensor descale amax / 448 and rounded to E4M3
+    (torch.float8_e4m3fn, round to nearest even).  Returns (q, k, v codes,
+    (q_descale, k_descale, v_descale)); the value of an element is its code
+    times its tensor's descale."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    xs = [_normal(gen, (B, Hq, Nq, d)), _normal(gen, (B, Hkv, Nk, d)), _normal(gen, (B, Hkv, Nk, d))]
+    out, desc = [], []
+    for x in xs:
+        ds = float(x.abs().max()) / 448.0
+        out.append((x / ds).to(torch.float8_e4m3fn))
+        desc.append(ds)
+    return out[0], out[1], out[2], tuple(desc)
 
 
 def make_prefill_inputs(B, Hq, Hkv, Nq, seq_lens, d, dtype: str, seed: int, block_size: int = 16,
