@@ -9,9 +9,12 @@
 // share a K/V head, so they are processed together against each page.
 //
 // decode_split: every wave is one split of one (sequence, K/V head, group of
-//   up to 16 query heads).  It walks its pages two at a time through a
-//   private double-buffered LDS ring (bounds-checked buffer-to-LDS loads, one
-//   descriptor per page, so token slots past the sequence end read as zero):
+//   up to 16 query heads).  It walks its pages two at a time, double-buffered
+//   (bounds-checked loads, one descriptor per page, so token slots past the
+//   sequence end read as zero): K goes straight into registers in the A
+//   operand layout of the score product, V through a private LDS ring for
+//   the transposing reads.  Keeping K out of LDS halves the ring, so two
+//   work-groups fit on a compute unit and twice the pages are in flight:
 //     Sᵀ = K_page Qᵀ          (16 tokens x 16 query heads, 16x16x32 MFMA)
 //     online softmax per query head (running max m, running sum l, log2 domain)
 //     Oᵀ = Oᵀ exp2(m_old - m_new) + Vᵀ Pᵀ   (32 tokens per product; Vᵀ comes
@@ -49,11 +52,10 @@ struct DecCfg {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kPageBytes = kPage * kRowBytes;
   static constexpr int kSlices = kPageBytes / 1024;  // 1 KiB wave loads per page
-  static constexpr int kStageBytes = 4 * kPageBytes;  // K and V of two pages
-  static constexpr int kWaveBytes = 2 * kStageBytes;  // double buffer
-  static constexpr int kLds = kWaves * kWaveBytes;
+  static constexpr int kStageBytes = 2 * kPageBytes;  // V of two pages
   static constexpr int kKS = D / 32;               // 32-wide k blocks along d
   static constexpr int kDT = D / 16;               // 16-row M tiles of Oᵀ
+  static constexpr int kPairOps = 2 * (kKS + kSlices);  // memory operations per page pair
   static_assert(kSlices >= 1 && kSlices * 1024 == kPageBytes, "page must split into 1 KiB loads");
 };
 
@@ -70,14 +72,18 @@ struct SplitParams {
 // scalar loads: a vector load would make the wave wait for every outstanding
 // page load (they share one counter) and stall the pipeline each page.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const int* __restrict__ block_table,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(SplitParams p, const int* __restrict__ block_table,
                                                            const int* __restrict__ seq_lens,
                                                            float* __restrict__ part) {
   using C = DecCfg<T, D>;
   using TT = Tile<C::kRowBytes>;
   typedef typename Elem<T>::Frag Frag;
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::kLds];
+  // The two stages of every wave's V ring are separate LDS objects: the
+  // compiler then sees that the pair being loaded never aliases the pair
+  // being read, and lets the loads stay in flight across the reads.
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::kWaves * C::kStageBytes], v_st1[C::kWaves * C::kStageBytes];
   const int lane = lane_id(), w = wave_id();
   const int unit = blockIdx.x * C::kWaves + w;  // (split, query column tile) of this wave
   if (unit >= p.splits * p.n_qc) return;         // no barriers in this kernel
@@ -85,7 +91,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
   const int bhk = blockIdx.y;
   const int b = bhk / p.Hkv, hkv = bhk - b * p.Hkv;
   const int g = p.Hq / p.Hkv;
-  lds_char* ring = (lds_char*)smem_raw + w * C::kWaveBytes;
+  lds_char* const ring0 = (lds_char*)v_st0 + w * C::kStageBytes;
+  lds_char* const ring1 = (lds_char*)v_st1 + w * C::kStageBytes;
 
   const int i16 = lane & 15, G = lane >> 4;
   const int qi = qc * 16 + i16;                  // query head within the group (column)
@@ -99,10 +106,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
   const int tok_end = min(seq_len, pg1 * C::kPage);
   const int* table = block_table + (size_t)b * p.max_blocks;
 
-  // Stage pages pg, pg+1 (K then V) into ring buffer `st`.  Pages at or past
-  // pg1 get an empty range, slots past the sequence end are clipped.
-  auto load_pair = [&](int pg, int st) {
-    lds_char* sb = ring + st * C::kStageBytes;
+  // Stage pages pg, pg+1: K into kr (lane: token row i16, d = 32ks + 8G ..
+  // +7 of each page), V into ring buffer `st`.  Pages at or past pg1 get an
+  // empty range, slots past the sequence end are clipped.
+  typedef u32x4 KRegs[2][C::kKS];
+  auto load_pair = [&](int pg, int st, KRegs& kr) __attribute__((always_inline)) {
+    lds_char* sb = st ? ring1 : ring0;
 #pragma unroll
     for (int u = 0; u < 2; u++) {
       const int page_idx = pg + u;
@@ -118,18 +127,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
       const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.kc + base, bytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.vc + base, bytes);
 #pragma unroll
+      for (int ks = 0; ks < C::kKS; ks++) kr[u][ks] = buf_load16(rk, (uint32_t)i16 * C::kRowBytes + (4 * ks + G) * 16);
+#pragma unroll
       for (int i = 0; i < C::kSlices; i++) {
         const int s = i * 64 + lane;
         const int row = s / TT::kChunks, pc = s % TT::kChunks;
         const uint32_t off = row * C::kRowBytes + ((pc ^ TT::key(row)) << 4);
-        buf_load16_to_lds(rk, off, sb + u * C::kPageBytes + i * 1024);
-        buf_load16_to_lds(rv, off, sb + (2 + u) * C::kPageBytes + i * 1024);
+        buf_load16_to_lds(rv, off, sb + u * C::kPageBytes + i * 1024);
       }
     }
   };
 
   const int n_pairs = (pg1 - pg0 + 1) / 2;
-  if (n_pairs > 0) load_pair(pg0, 0);
+  KRegs ka, kb;  // K of the pair in stage 0 and in stage 1
+  load_pair(pg0, 0, ka);
 
   // Qᵀ as the B operand: column = query head, k = d (8 per lane per 32-wide block).
   Frag qf[C::kKS];
@@ -147,18 +158,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
   for (int dt = 0; dt < C::kDT; dt++) o[dt] = f32x4v{};
   float m = -INFINITY, l = 0.f;
 
-  for (int i = 0; i < n_pairs; i++) {
-    const int st = i & 1;
-    if (i + 1 < n_pairs) {
-      load_pair(pg0 + 2 * (i + 1), st ^ 1);
-      // Wait for the older stage only: the newer pair's loads may stay in flight.
-      // (A pair is 4 * kSlices loads; loads retire in issue order.)
-      wait_vmem_le<4 * C::kSlices>();
-    } else {
-      wait_vmem();
-    }
-    const lds_char* kb = ring + st * C::kStageBytes;
-    const lds_char* vb = kb + 2 * C::kPageBytes;
+  // One page pair: K from registers, V from ring stage st.
+  auto pair = [&](int i, int st, const KRegs& kr) __attribute__((always_inline)) {
+    const lds_char* vb = st ? ring1 : ring0;
     const int t0 = (pg0 + 2 * i) * C::kPage;  // first token of the pair
 
     // ---- Sᵀ for both pages: register r of page u holds token t0 + 16u + 4G + r.
@@ -167,10 +169,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
     for (int u = 0; u < 2; u++) {
       s[u] = f32x4v{};
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ks++) {
-        const Frag a = __builtin_bit_cast(Frag, lds_read16(kb + u * C::kPageBytes, TT::off(i16, 4 * ks + G)));
-        s[u] = Mma16<T>::mma(a, qf[ks], s[u]);
-      }
+      for (int ks = 0; ks < C::kKS; ks++) s[u] = Mma16<T>::mma(__builtin_bit_cast(Frag, kr[u][ks]), qf[ks], s[u]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -215,7 +214,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p, const 
       const i16x8 a8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       o[dt] = Mma16<T>::mma(__builtin_bit_cast(Frag, a8), pf, o[dt]);
     }
+  };
+
+  // Two pairs per trip so that both K register sets are compile-time objects.
+  // Before a pair is used, only the newer pair's loads may still be in flight
+  // (loads retire in issue order).  Loads and pairs past the split are issued
+  // anyway: their pages have empty ranges and their tokens lie past tok_end,
+  // so they add nothing, and no branch makes the waits conservative.
+  for (int i = 0; i < n_pairs; i += 2) {
+    load_pair(pg0 + 2 * (i + 1), 1, kb);
+    wait_vmem_le<C::kPairOps>();
+    pair(i, 0, ka);
+    load_pair(pg0 + 2 * (i + 2), 0, ka);
+    wait_vmem_le<C::kPairOps>();
+    pair(i + 1, 1, kb);
   }
+  wait_vmem();
 
   // ---- partial result: Oᵀ (unnormalised), m, l (summed over the 4 lane groups).
   l += __shfl_xor(l, 16, 64);

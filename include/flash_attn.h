@@ -190,9 +190,9 @@ int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Number of KV splits the decode uses for num_splits = 0 (automatic): enough
- * work-groups to cover the 256 compute units several times over, with at
- * least 4 pages per split.  Pure host arithmetic, no HIP call.
+ * Number of KV splits the decode uses for num_splits = 0 (automatic): about
+ * four splits (one per wave) per compute unit of the 256, with at least 4
+ * pages per split.  Pure host arithmetic, no HIP call.
  */
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size);
 

@@ -192,7 +192,7 @@ def test_workspace_queries(L):
     assert L.flash_attn_bwd_varlen_workspace_bytes(16, 16, 16, 35457, 35457, 4000, 4000, 128, BF16) == 2 * 16 * 35457 * 4
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 0, 10, 0, 10, 64, F16) == 0
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 10, 10, 11, 10, 64, F16) == 0
-    # Automatic split count: about 4 work-groups per compute unit, at least 4 pages per split.
+    # Automatic split count: about 4 splits per compute unit, at least 4 pages per split.
     assert L.flash_attn_decode_num_splits(8, 8, 2048, 16) == 16
     assert L.flash_attn_decode_num_splits(1, 1, 2, 16) == 1
     assert L.flash_attn_decode_num_splits(1, 1, 100000, 16) == 1024
