@@ -54,34 +54,46 @@ constexpr int kVtKeys = 64;  // keys per staged Vᵀ tile
 
 // ---------------------------------------------------------------------------
 // Pre-pass: Vt[b][hkv][tile][d][64] = V[b][hkv][64 * tile + key][d], zero past Nk.
+// Each thread moves a 4-key x 16-d block: four 16-byte row loads, four 4x4
+// byte transposes in registers (v_perm_b32), sixteen 4-byte stores.  Sixteen
+// consecutive threads cover the 64 keys of a tile, so every output row of Vᵀ
+// is written as one contiguous 64-byte run.
 // ---------------------------------------------------------------------------
+// Bytes j of a, b, c, d (j = 0..3) as one word, for each j: the transpose of a
+// 4x4 byte block held as four row words.
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t* o) {
+  // perm(x, y, sel): byte i of the result is byte sel_i of {x:y} (y = bytes 0-3, x = bytes 4-7).
+  const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);  // a0 b0 c0 d0
+  o[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);  // a1 b1 c1 d1
+  o[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);  // a2 b2 c2 d2
+  o[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);  // a3 b3 c3 d3
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ vt,
                                                      int Nk, int n_tiles) {
-  __shared__ uint8_t t[kVtKeys][D + 16];
+  constexpr int kBlocks = (kVtKeys / 4) * (D / 16);  // 4 x 16 blocks per tile
   const int tile = blockIdx.x;
   const size_t bh = blockIdx.y;
-  const uint8_t* src = v + bh * (size_t)Nk * D;
-  for (int c = threadIdx.x; c < kVtKeys * D / 16; c += 256) {
-    const int row = c / (D / 16), ch = c % (D / 16);
-    const int key = tile * kVtKeys + row;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < Nk) val = *(const u32x4*)(src + (size_t)key * D + 16 * ch);
-#pragma unroll
-    for (int i = 0; i < 4; i++) *(uint32_t*)&t[row][16 * ch + 4 * i] = val[i];
-  }
-  __syncthreads();
+  const __amdgpu_buffer_rsrc_t src = make_rsrc(v + bh * (size_t)Nk * D, (uint32_t)Nk * D);
   uint8_t* dst = vt + (bh * n_tiles + tile) * (size_t)(D * kVtKeys);
-  for (int c = threadIdx.x; c < D * kVtKeys / 16; c += 256) {
-    const int d = c / (kVtKeys / 16), kc = c % (kVtKeys / 16);
-    u32x4 w;
+  for (int t = threadIdx.x; t < kBlocks; t += 256) {
+    const int kg = t % (kVtKeys / 4), dg = t / (kVtKeys / 4);
+    const int key0 = tile * kVtKeys + 4 * kg, d0 = 16 * dg;
+    u32x4 r[4];  // rows key0 .. key0+3, bytes d0 .. d0+15 (zero past Nk)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int k0 = 16 * kc + 4 * i;
-      w[i] = (uint32_t)t[k0][d] | ((uint32_t)t[k0 + 1][d] << 8) | ((uint32_t)t[k0 + 2][d] << 16) |
-             ((uint32_t)t[k0 + 3][d] << 24);
+    for (int i = 0; i < 4; i++) r[i] = buf_load16(src, (uint32_t)(key0 + i) * D + d0);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      uint32_t o[4];
+      transpose4x4(r[0][c], r[1][c], r[2][c], r[3][c], o);
+#pragma unroll
+      for (int j = 0; j < 4; j++) *(uint32_t*)(dst + (size_t)(d0 + 4 * c + j) * kVtKeys + 4 * kg) = o[j];
     }
-    *(u32x4*)(dst + (size_t)d * kVtKeys + 16 * kc) = w;
   }
 }
 
