@@ -26,7 +26,7 @@ report (see `profiles/`):
   python bench.py --traffic-from FETCH.csv WRITE.csv
       turns the two counter CSVs into profiles/traffic.json (bytes per launch,
       scaled by the copy's known bytes, tagged with the kernels' source hash)
-      and profiles/hbm_traffic_mha_bf16_4k_and_decode.md.
+      and profiles/hbm_traffic_mha_bf16_4k_decode_fp8.md.
 """
 
 from __future__ import annotations
@@ -99,7 +99,7 @@ def source_hash(*names) -> str:
 
 
 KERNEL_SOURCES = {"fwd": ("fa_fwd.hip",), "prep": ("fa_bwd.hip",), "dkdv": ("fa_bwd.hip",), "dq": ("fa_bwd.hip",),
-                  "decode": ("fa_decode.hip",)}
+                  "decode": ("fa_decode.hip",), "fp8": ("fa_fwd_fp8.hip",)}
 
 
 def measured_traffic(kernel: str):
@@ -311,6 +311,11 @@ def profile_once(torch, fa, si):
     fa.decode_paged(*args)
     torch.cuda.synchronize()
     del args
+    wf = si.WORKLOADS["mha_fp8_4k"]
+    q, k, v, desc = si.make_fp8_inputs(wf.B, wf.Hq, wf.Hkv, wf.Nq, wf.Nk, wf.d, wf.seed)
+    fa.fwd_fp8(q.to("cuda"), k.to("cuda"), v.to("cuda"), *desc, causal=True)
+    torch.cuda.synchronize()
+    del q, k, v
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     b.copy_(a)
@@ -321,7 +326,8 @@ def profile_once(torch, fa, si):
 COPY_BYTES = 1 << 30
 # rocprofv3 kernel names -> the keys used above (the decode is split + reduce).
 KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_kernel", "dkdv"), ("bwd_dkdv16_kernel", "dkdv"),
-               ("bwd_dq_kernel", "dq"), ("decode_split_kernel", "decode"), ("decode_reduce_kernel", "decode"))
+               ("bwd_dq_kernel", "dq"), ("decode_split_kernel", "decode"), ("decode_reduce_kernel", "decode"),
+               ("fp8_vt_kernel", "fp8"), ("fwd_fp8_kernel", "fp8"))
 
 
 def _counter_sums(path, counter):
@@ -372,7 +378,8 @@ def traffic_from(fetch_csv, write_csv):
     w = None
     lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
              "Workloads: mha_bf16_4k (B=2, H=16, N=4096, d=128, causal, bf16) for fwd / prep / dkdv / dq;",
-             "decode_gqa_paged (B=8, Hq=32, Hkv=8, Nk=32768, d=128, bf16, 16-token pages) for decode.", "",
+             "decode_gqa_paged (B=8, Hq=32, Hkv=8, Nk=32768, d=128, bf16, 16-token pages) for decode;",
+             "mha_fp8_4k (B=2, H=16, N=4096, d=128, causal, E4M3 in, bf16 out) for fp8 (V staging + forward).", "",
              "Commands (from the repository root, on the GPU):", "",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- python3 bench.py --profile-once",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- python3 bench.py --profile-once",
@@ -382,11 +389,11 @@ def traffic_from(fetch_csv, write_csv):
              f"{max(fcopy):.0f} KiB fetched and {max(wcopy):.0f} KiB written, so fetch counts scale by {f_factor:.4f} "
              f"and write counts by {w_factor:.4f}.", "",
              "| kernel | fetch bytes | write bytes | total per launch |", "|---|---:|---:|---:|"]
-    for key in ("fwd", "prep", "dkdv", "dq", "decode"):
+    for key in ("fwd", "prep", "dkdv", "dq", "decode", "fp8"):
         if key in rec:
             r = rec[key]
             lines.append(f"| {key} | {r['fetch_bytes']:,} | {r['write_bytes']:,} | {r['hbm_bytes_per_launch']:,} |")
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic_mha_bf16_4k_and_decode.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_mha_bf16_4k_decode_fp8.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
 
@@ -492,7 +499,7 @@ def main(argv=None):
                                "descales, bf16 O", "us": round(ms_f * 1e3, 2), "TFLOP/s": round(tf, 2),
                    "roofline": {"kernel": "fwd_fp8 (V staging + forward)", "bound": "mfma", "achieved": round(tf, 2),
                                 "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_FP8, 4),
-                                "traffic": None}}
+                                "traffic": measured_traffic("fp8")}}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)
