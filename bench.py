@@ -14,7 +14,7 @@ roof, and the float64 CPU oracle on a bounded sample of the training
 workload (its `cpu_baseline` leg; the only place this file touches the
 oracle).
 
-Prints one JSON line.  `--gpus` above 1 is refused: this build runs on a
+Prints one JSON line.  `--gpus` above 1 is refused: the library is measured on a
 single GPU.
 
 Two helper modes produce the measured HBM traffic that the roofline objects
@@ -380,10 +380,10 @@ def traffic_from(fetch_csv, write_csv):
              "Workloads: mha_bf16_4k (B=2, H=16, N=4096, d=128, causal, bf16) for fwd / prep / dkdv / dq;",
              "decode_gqa_paged (B=8, Hq=32, Hkv=8, Nk=32768, d=128, bf16, 16-token pages) for decode;",
              "mha_fp8_4k (B=2, H=16, N=4096, d=128, causal, E4M3 in, bf16 out) for fp8 (V staging + forward).", "",
-             "Commands (from the repository root, on the GPU):", "",
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- python3 bench.py --profile-once",
-             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- python3 bench.py --profile-once",
-             "    python3 bench.py --traffic-from gpurun_out/pmc_fetch/p_counter_collection.csv gpurun_out/pmc_write/p_counter_collection.csv",
+             "Commands (from the repository root, on the GPU; $OUT is any output directory):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o p -- python3 bench.py --profile-once",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o p -- python3 bench.py --profile-once",
+             "    python3 bench.py --traffic-from $OUT/pmc_fetch/p_counter_collection.csv $OUT/pmc_write/p_counter_collection.csv",
              "",
              f"Calibration: a {COPY_BYTES >> 20} MiB device copy reads and writes {COPY_BYTES} bytes; the counters report "
              f"{max(fcopy):.0f} KiB fetched and {max(wcopy):.0f} KiB written, so fetch counts scale by {f_factor:.4f} "
