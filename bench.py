@@ -102,6 +102,20 @@ KERNEL_SOURCES = {"fwd": ("fa_fwd.hip",), "prep": ("fa_bwd.hip",), "dkdv": ("fa_
                   "decode": ("fa_decode.hip",), "fp8": ("fa_fwd_fp8.hip",)}
 
 
+def measured_util(kernel: str):
+    """Counter-based MFMA busy fraction, shader clock and LDS bank conflicts of
+    one launch, from the committed rocprofv3 summary, or None when there is
+    none or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", "mfma_util.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(*KERNEL_SOURCES[kernel]):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "clock_ghz", "lds_bank_conflicts_per_access")}
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel's source changed since."""
@@ -344,6 +358,41 @@ def _counter_sums(path, counter):
     return out
 
 
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+SIMDS, XCDS = 1024, 8
+
+
+def util_from(csv_path):
+    """profiles/mfma_util.json from one rocprofv3 counter CSV of --profile-once:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x SIMDs)
+    (rocprofv3's MfmaUtil), clock = GRBM_GUI_ACTIVE per XCD / duration, LDS bank
+    conflicts per access = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - conflicts)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {},
+                                                       "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rec = {"_definition": util_from.__doc__.split("\n", 1)[1].strip()}
+    for d in per.values():
+        key = next((k for pat, k in KERNEL_KEYS if pat in d["name"]), None)
+        if key is None or key in rec:
+            continue
+        c = d["c"]
+        if "decode_reduce" in d["name"] or "fp8_vt" in d["name"]:
+            continue  # the key's dominant kernel is reported (split / forward)
+        grbm = c["GRBM_GUI_ACTIVE"] / XCDS
+        rec[key] = {"mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm * SIMDS), 4),
+                    "clock_ghz": round(grbm / (d["us"] * 1e3), 3),
+                    "lds_bank_conflicts_per_access": round(
+                        c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"]), 4),
+                    "us": round(d["us"], 2), "source_hash": source_hash(*KERNEL_SOURCES[key])}
+    with open(os.path.join(ROOT, "profiles", "mfma_util.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def traffic_from(fetch_csv, write_csv):
     fetch, write = _counter_sums(fetch_csv, "FETCH_SIZE"), _counter_sums(write_csv, "WRITE_SIZE")
     def per_key(rows):
@@ -407,11 +456,16 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-once", action="store_true", help="launch every kernel once (for rocprofv3 counters)")
+    ap.add_argument("--util-from", metavar="COUNTER_CSV",
+                    help="write profiles/mfma_util.json from a rocprofv3 counter CSV of --profile-once")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return 0
+    if args.util_from:
+        util_from(args.util_from)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention kernels here are "
@@ -445,7 +499,8 @@ def main(argv=None):
         else:
             ach, peak, unit = amount / (ms * 1e-3) / 1e9, PEAK_HBM, "GB/s"
         return {"kernel": name, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": measured_traffic(name), "avg_us": round(ms * 1e3, 2)}
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(name), "avg_us": round(ms * 1e3, 2),
+                "counters": measured_util(name)}
 
     dominant = max(per, key=per.get)
     line = {
@@ -499,7 +554,7 @@ def main(argv=None):
                                "descales, bf16 O", "us": round(ms_f * 1e3, 2), "TFLOP/s": round(tf, 2),
                    "roofline": {"kernel": "fwd_fp8 (V staging + forward)", "bound": "mfma", "achieved": round(tf, 2),
                                 "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_FP8, 4),
-                                "traffic": measured_traffic("fp8")}}
+                                "traffic": measured_traffic("fp8"), "counters": measured_util("fp8")}}
     if not args.no_decode:
         wd, ms_dec = bench_decode(torch, fa, si, args.steps, args.warmup)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.seq_len, wd.d, 2)
