@@ -40,6 +40,9 @@ int check_varlen(int B, int Hq, int Hkv, int total_q, int total_k, int max_q, in
   if (!headdim_ok(d)) return FA_ERR_HEADDIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   if ((int64_t)Hq * total_q * d >= kMaxElems || (int64_t)Hkv * total_k * d >= kMaxElems) return FA_ERR_SHAPE;
+  // One (sequence, head) slab is addressed with 32-bit byte offsets.
+  if ((int64_t)max_q * d * elem_bytes(dtype) >= kMaxElems || (int64_t)max_k * d * elem_bytes(dtype) >= kMaxElems)
+    return FA_ERR_SHAPE;
   // Grids span (sequence, head, tile of the longest sequence); keep them and B + 1 in 32 bits.
   if ((int64_t)B * Hq * ((max_q + 127) / 128 + 1) >= kMaxElems ||
       (int64_t)B * Hkv * ((max_k + 127) / 128 + 1) >= kMaxElems)

@@ -162,7 +162,8 @@ int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* d
  * queries gives dK = dV = 0.  max_seqlen_q / max_seqlen_k bound every n_b
  * (the grids are sized by them) and may not exceed total_q / total_k.
  * Sizes: B, Hq, Hkv >= 1; total_q, total_k, max_seqlen_q, max_seqlen_k >= 0;
- * Hq*total_q*d and Hkv*total_k*d below 2^31 elements.
+ * Hq*total_q*d and Hkv*total_k*d below 2^31 elements; max_seqlen * d below
+ * 2^31 bytes (one sequence's slab of one head).
  * The cumulative arrays live on the device, so the host cannot check them:
  * a sequence whose entries break the ordering above or exceed the bounds is
  * skipped (its output rows are left unwritten) and no access leaves the

@@ -120,6 +120,8 @@ VARLEN_CASES = [
     (dict(d=80), HEADDIM), (dict(Hq=6, Hkv=4), GQA),
     (dict(tq=1 << 22, mq=10), SHAPE), (dict(Hkv=4, tk=1 << 22, mk=10), SHAPE),
     (dict(B=1 << 28, tq=100, mq=100), SHAPE),
+    # one sequence's slab past 2^31 bytes (float32, Hq = Hkv = 1)
+    (dict(dtype=F32, Hq=1, Hkv=1, tq=1 << 22, mq=1 << 22, causal=0), SHAPE),
     (dict(scale=NAN), SCALE),
     (dict(), ALIGN), (dict(tq=0, mq=0, tk=0, mk=0), ALIGN), (dict(dtype=F32, causal=0), ALIGN),
 ]
