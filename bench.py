@@ -358,8 +358,7 @@ def _counter_sums(path, counter):
     return out
 
 
-UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
-SIMDS, XCDS = 1024, 8
+SIMDS, XCDS = 1024, 8  # MI355X: 256 compute units x 4 SIMDs, 8 XCDs
 
 
 def util_from(csv_path):
@@ -376,12 +375,14 @@ def util_from(csv_path):
             d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     rec = {"_definition": util_from.__doc__.split("\n", 1)[1].strip()}
     for d in per.values():
+        # One launch per key: the first dispatch of its main kernel (the decode's
+        # split kernel, the FP8 forward rather than its V staging).
+        if "decode_reduce" in d["name"] or "fp8_vt" in d["name"]:
+            continue
         key = next((k for pat, k in KERNEL_KEYS if pat in d["name"]), None)
         if key is None or key in rec:
             continue
         c = d["c"]
-        if "decode_reduce" in d["name"] or "fp8_vt" in d["name"]:
-            continue  # the key's dominant kernel is reported (split / forward)
         grbm = c["GRBM_GUI_ACTIVE"] / XCDS
         rec[key] = {"mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm * SIMDS), 4),
                     "clock_ghz": round(grbm / (d["us"] * 1e3), 3),
