@@ -8,17 +8,20 @@ backward is launched as its three phases (row terms, dK/dV, dQ) so that HIP
 events on the library's stream time every kernel of the step separately;
 the roofline object describes whichever kernel takes the most time.
 
-The same run also times the split-KV paged decode workload (B=8, Hq=32,
-Hkv=8, 32768 cached tokens per sequence, 16-token pages) against the HBM
-roof, and the float64 CPU oracle on a bounded sample of the training
-workload (its `cpu_baseline` leg; the only place this file touches the
-oracle).
+The same run also times, each reported under its own key: the same step on
+the grouped-query shape (`gqa`), on a packed batch of variable-length
+sequences (`varlen`), a chunked prefill over a paged KV cache
+(`prefill_paged`), the FP8 (E4M3) forward (`fp8`), the split-KV paged decode
+workload (B=8, Hq=32, Hkv=8, 32768 cached tokens per sequence, 16-token
+pages) against the HBM roof (`decode`), and the float64 CPU oracle on a
+bounded sample of the training workload (its `cpu_baseline` leg; the only
+place this file touches the oracle).
 
 Prints one JSON line.  `--gpus` above 1 is refused: the library is measured on a
 single GPU.
 
-Two helper modes produce the measured HBM traffic that the roofline objects
-report (see `profiles/`):
+Helper modes produce the measured HBM traffic and counter figures that the
+roofline objects report (see `profiles/`):
   python bench.py --profile-once
       runs every kernel of the step and the decode once, plus a 1 GiB device
       copy whose byte count calibrates the counters; run it under
@@ -26,7 +29,10 @@ report (see `profiles/`):
   python bench.py --traffic-from FETCH.csv WRITE.csv
       turns the two counter CSVs into profiles/traffic.json (bytes per launch,
       scaled by the copy's known bytes, tagged with the kernels' source hash)
-      and profiles/hbm_traffic_mha_bf16_4k_decode_fp8.md.
+      and profiles/hbm_traffic_mha_bf16_4k_decode_fp8.md;
+  python bench.py --util-from COUNTERS.csv
+      turns a counter CSV of --profile-once (MFMA busy cycles, GRBM active
+      cycles, LDS bank conflicts) into profiles/mfma_util.json.
 """
 
 from __future__ import annotations
