@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_BF16 = 2516.6  # TFLOP/s: 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_MFMA_FP8 = 5033.2   # TFLOP/s: dense fp8, twice the bf16 rate
+PEAK_MFMA_F32 = 157.3    # TFLOP/s: dense fp32 matrix cores
 PEAK_HBM = 8000.0        # GB/s: MI355X HBM3E
 METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4096, d=128, causal) + % of MFMA peak"
 
@@ -144,15 +145,15 @@ def ensure_library():
         build.build()
 
 
-def bench_training(torch, fa, si, steps, warmup, name="mha_bf16_4k"):
+def bench_training(torch, fa, si, steps, warmup, name="mha_bf16_4k", causal=True):
     w = si.WORKLOADS[name]
     q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, fa.FA_BF16), dtype=torch.uint8,
+    code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w.dtype]
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, code), dtype=torch.uint8,
                      device="cuda")
-    causal = True
 
     def step(ev=None):
         if ev: ev[0].record()
@@ -532,6 +533,19 @@ def main(argv=None):
     line["gqa"] = {"workload": "gqa_bf16_4k: causal forward + backward, B=2 Hq=32 Hkv=8 N=4096 d=128 bf16",
                    "TFLOP/s": round((flg["fwd"] + flg["dkdv"] + flg["dq"]) / (ms_g * 1e-3) / 1e12, 2),
                    "ms_per_step": round(ms_g, 4), "us": {n: round(v * 1e3, 2) for n, v in per_g.items()}}
+    # The other attention configurations, same step, each against its dtype's matrix peak.
+    line["configs"] = {}
+    for cname, causal in (("mha_f32_small", False), ("mha_f16", True), ("mha_f16", False), ("mha_bf16_16k", True)):
+        wc, ms_c, per_c, _ = bench_training(torch, fa, si, args.steps, args.warmup, cname, causal)
+        flc = attention_flops(wc.B, wc.Hq, wc.Nq, wc.Nk, wc.d, causal)
+        peak = PEAK_MFMA_F32 if wc.dtype == "f32" else PEAK_MFMA_BF16
+        fwd_tf = flc["fwd"] / (per_c["fwd"] * 1e-3) / 1e12
+        bwd_tf = (flc["dkdv"] + flc["dq"]) / ((per_c["prep"] + per_c["dkdv"] + per_c["dq"]) * 1e-3) / 1e12
+        line["configs"][f"{cname}_{'causal' if causal else 'noncausal'}"] = {
+            "shape": f"B={wc.B} H={wc.Hq} N={wc.Nq} d={wc.d} {wc.dtype}" + (f" Q,K x{wc.qk_mult:g}" if wc.qk_mult != 1 else ""),
+            "fwd_us": round(per_c["fwd"] * 1e3, 2), "bwd_us": round((per_c["prep"] + per_c["dkdv"] + per_c["dq"]) * 1e3, 2),
+            "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2), "peak": peak,
+            "fwd_frac": round(fwd_tf / peak, 4), "bwd_frac": round(bwd_tf / peak, 4)}
     # Packed variable-length batch (16 causal sequences of seeded lengths), same step.
     wv, lens_v, ms_v, per_v = bench_varlen(torch, fa, si, args.steps, args.warmup)
     flv = {"fwd": 0, "dkdv": 0, "dq": 0}
