@@ -26,6 +26,11 @@
 // softmax of its last S.  Group 1 runs one slot behind group 0, so every SIMD
 // always has one MFMA-phase wave and one VALU-phase wave.
 //
+// Grids with fewer than two 256-row work-groups per compute unit (short
+// sequences, few heads) run the same kernel with 4 waves (128 rows) per
+// work-group, so that the chip fills; the two groups are then waves 0-1 and
+// 2-3, and a SIMD's two waves come from two work-groups.
+//
 // The running max moves only when a row's scores exceed it by more than 2^8
 // (conditional rescaling, named on the concept page "Flash-Attention" among
 // FlashAttention-4's techniques, "Known limits"); O and l share the stale max,
@@ -53,9 +58,9 @@ __device__ __forceinline__ void sched_pv_s() {
   __builtin_amdgcn_sched_group_barrier(kMfma, 2 * pd, 0);
 }
 
-template <typename T, int D>
+template <typename T, int D, int W = 8>
 struct FwdCfg {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = W;                           // 8, or 4 for small grids
   static constexpr int kBR = 32 * kWaves;                    // query rows per work-group
   static constexpr int kES = Elem<T>::kBytes;
   static constexpr int kRowBytes = D * kES;
@@ -89,10 +94,10 @@ constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
 
 // PAGED: K and V are read from a paged cache through the block table; the
 // queries are the last Nq positions of each sequence (dense Q, O, LSE).
-template <typename T, int D, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, bool CAUSAL, bool PAGED, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __restrict__ seq_lens) {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, W>;
   using E = Elem<T>;
   using F = Frags<T>;
   using TT = Tile<C::kRowBytes>;
@@ -363,7 +368,7 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
   // of group G runs phase u = t - G: even u = GEMM of tile u/2 (PV of tile
   // u/2 - 1, then S of tile u/2), odd u = softmax of tile (u-1)/2.  Slots
   // are unrolled by 4 so every buffer parity is a compile-time constant.
-  const int G = w >> 2;
+  const int G = w / (C::kWaves / 2);
   const int n_slots = (2 * n_tiles + 2 + 3) & ~3;
 
   auto slot = [&](auto gc, auto pc, int t) __attribute__((always_inline)) {
@@ -448,9 +453,9 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool PAGED>
+template <typename T, int D, bool CAUSAL, bool PAGED, int W>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, W>;
   FwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
@@ -460,23 +465,33 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;  // a packed batch with no query
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, PAGED>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, PAGED, W>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,
                      a.block_table, a.seq_lens);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int W>
 hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
-  if (a.block_table) return a.causal ? launch_typed<T, D, true, true>(a, s) : launch_typed<T, D, false, true>(a, s);
-  return a.causal ? launch_typed<T, D, true, false>(a, s) : launch_typed<T, D, false, false>(a, s);
+  if (a.block_table)
+    return a.causal ? launch_typed<T, D, true, true, W>(a, s) : launch_typed<T, D, false, true, W>(a, s);
+  return a.causal ? launch_typed<T, D, true, false, W>(a, s) : launch_typed<T, D, false, false, W>(a, s);
+}
+
+constexpr int kCUs = 256;  // MI355X compute units
+
+// 8-wave work-groups unless that grid gives fewer than two per compute unit.
+template <typename T, int D>
+hipError_t launch_waves(const FwdArgs& a, hipStream_t s) {
+  const int64_t grid8 = (int64_t)((a.Nq + FwdCfg<T, D, 8>::kBR - 1) / FwdCfg<T, D, 8>::kBR) * a.B * a.Hq;
+  return grid8 < 2 * kCUs ? launch_mask<T, D, 4>(a, s) : launch_mask<T, D, 8>(a, s);
 }
 
 template <typename T>
 hipError_t launch_dtype(const FwdArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 32: return launch_mask<T, 32>(a, s);
-    case 64: return launch_mask<T, 64>(a, s);
-    case 128: return launch_mask<T, 128>(a, s);
+    case 32: return launch_waves<T, 32>(a, s);
+    case 64: return launch_waves<T, 64>(a, s);
+    case 128: return launch_waves<T, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
