@@ -52,7 +52,7 @@ def test_header_declares_the_entry_points():
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_decode_paged", "flash_attn_strerror",
               "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits",
               "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes",
-              "flash_attn_prefill_paged"):
+              "flash_attn_prefill_paged", "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_workspace_bytes"):
         assert n in names
 
 
@@ -188,12 +188,35 @@ def test_prefill_validation(L, kw, code):
     assert pre(L, **kw) == code
 
 
+def fp8(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=128, Nk=200, d=128, scale=0.1, qd=1.0, kd=1.0, vd=1.0,
+        causal=1, ws=P, ws_bytes=1 << 20):
+    return L.flash_attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, qd, kd, vd, causal, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(v=None), NULL), (dict(lse=None), NULL),
+    (dict(B=0), SHAPE), (dict(Nq=0), SHAPE), (dict(Nk=-1), SHAPE),
+    (dict(d=32), HEADDIM), (dict(d=96), HEADDIM), (dict(Hq=6, Hkv=4), GQA),
+    (dict(B=70000, Hkv=1, Hq=1, Nq=1, Nk=1), SHAPE),   # the staging grid's second dimension
+    (dict(Nq=1 << 24, B=1, Hq=1, Hkv=1), SHAPE),
+    (dict(scale=NAN), SCALE), (dict(qd=INF), SCALE), (dict(vd=NAN), SCALE), (dict(scale=1e30, qd=1e30), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=2 * 4 * 64 * 128 - 1, B=1, Hkv=2, Nk=200), WORKSPACE),
+    (dict(), ALIGN), (dict(causal=0, d=64), ALIGN),
+])
+def test_fwd_fp8_validation(L, kw, code):
+    assert fp8(L, **kw) == code
+
+
 def test_workspace_queries(L):
     assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 128, BF16) == 2 * 2 * 16 * 4096 * 4
     assert L.flash_attn_bwd_workspace_bytes(2, 16, 16, 4096, 4096, 96, BF16) == 0
     assert L.flash_attn_bwd_varlen_workspace_bytes(16, 16, 16, 35457, 35457, 4000, 4000, 128, BF16) == 2 * 16 * 35457 * 4
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 0, 10, 0, 10, 64, F16) == 0
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 10, 10, 11, 10, 64, F16) == 0
+    # FP8: V staged transposed in 64-key tiles, one byte per element.
+    assert L.flash_attn_fwd_fp8_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 128
+    assert L.flash_attn_fwd_fp8_workspace_bytes(1, 2, 200, 64) == 1 * 2 * 256 * 64
+    assert L.flash_attn_fwd_fp8_workspace_bytes(1, 2, 200, 32) == 0
     # Automatic split count: about 4 splits per compute unit, at least 4 pages per split.
     assert L.flash_attn_decode_num_splits(8, 8, 2048, 16) == 16
     assert L.flash_attn_decode_num_splits(1, 1, 2, 16) == 1
