@@ -106,6 +106,33 @@ def _dense(name: str, t: torch.Tensor, dtype=None, ndim=None) -> torch.Tensor:
     return t
 
 
+def _out(name: str, t, shape, dtype, device: torch.device) -> torch.Tensor:
+    """A caller-provided output checked against the shape the kernels write, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dense(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _workspace(t, nbytes: int, device: torch.device) -> torch.Tensor:
+    """A caller-provided workspace (its size is checked by the library), or a new one."""
+    if t is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return _dense("workspace", t)
+
+
+def _one_device(**tensors) -> torch.device:
+    """The device of the first tensor; every other one must be on it."""
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    first = next(iter(devs.values()))
+    for n, dv in devs.items():
+        if dv != first:
+            raise ValueError(f"{n} is on {dv}, the other tensors on {first}")
+    return first
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
@@ -125,9 +152,9 @@ def fwd(q, k, v, causal: bool = False, scale=None, out=None, lse=None):
     Hkv, Nk = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
         raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
-    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
-        _dense("lse", lse, torch.float32)
+    dev = _one_device(q=q, k=k, v=v, out=out, lse=lse)
+    out = _out("out", out, (B, Hq, Nq, d), q.dtype, dev)
+    lse = _out("lse", lse, (B, Hq, Nq), torch.float32, dev)
     code = lib().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                                 _default_scale(d, scale), int(bool(causal)), _dtype_code(q), _stream(q.device))
     _check(code, "flash_attn_fwd")
@@ -146,13 +173,17 @@ def bwd(q, k, v, out, dout, lse, causal: bool = False, scale=None, dq=None, dk=N
     _dense("lse", lse, torch.float32, 3)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    dq = torch.empty_like(q) if dq is None else _dense("dq", dq, q.dtype)
-    dk = torch.empty_like(k) if dk is None else _dense("dk", dk, q.dtype)
-    dv = torch.empty_like(v) if dv is None else _dense("dv", dv, q.dtype)
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError(f"out {tuple(out.shape)}, dout {tuple(dout.shape)} or lse {tuple(lse.shape)} "
+                         f"do not match q {tuple(q.shape)}")
+    dev = _one_device(q=q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    dq = _out("dq", dq, q.shape, q.dtype, dev)
+    dk = _out("dk", dk, k.shape, q.dtype, dev)
+    dv = _out("dv", dv, v.shape, q.dtype, dev)
     code_dt = _dtype_code(q)
-    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, code_dt)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, code_dt), dev)
     code = lib().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                                 _ptr(dv), B, Hq, Hkv, Nq, Nk, d, _default_scale(d, scale), int(bool(causal)), code_dt,
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
@@ -164,6 +195,11 @@ def bwd_phase(phase: str, q, k, v, out, dout, lse, dq, dk, dv, workspace, causal
     """Run one backward phase ('preprocess', 'dkdv' or 'dq') on torch's current
     stream; the outputs and the workspace are caller-allocated.  Arguments not
     used by the phase may be None."""
+    given = dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    for name, t in given.items():
+        if t is not None:
+            _dense(name, t)
+    _one_device(**given)
     ref = q if q is not None else out
     B, Hq, Nq, d = ref.shape
     Hkv, Nk = (k.shape[1], k.shape[2]) if k is not None else (Hq, Nq)
@@ -206,9 +242,9 @@ def fwd_varlen(q, k, v, cu_q, cu_k, hq: int, hkv: int, max_seqlen_q: int, max_se
     _dense("v", v, q.dtype, 2)
     if v.shape != k.shape:
         raise ValueError(f"v shape {tuple(v.shape)} does not match k {tuple(k.shape)}")
-    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
-    lse = torch.empty(q.shape[0], dtype=torch.float32, device=q.device) if lse is None else \
-        _dense("lse", lse, torch.float32)
+    dev = _one_device(q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k, out=out, lse=lse)
+    out = _out("out", out, q.shape, q.dtype, dev)
+    lse = _out("lse", lse, (q.shape[0],), torch.float32, dev)
     code = lib().flash_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
                                        B, hq, hkv, tq, tk, mq, mk, d, _default_scale(d, scale), int(bool(causal)),
                                        _dtype_code(q), _stream(q.device))
@@ -228,13 +264,16 @@ def bwd_varlen(q, k, v, out, dout, lse, cu_q, cu_k, hq: int, hkv: int, max_seqle
     for name, t in (("v", v), ("out", out), ("dout", dout)):
         _dense(name, t, q.dtype, 2)
     _dense("lse", lse, torch.float32, 1)
-    dq = torch.empty_like(q) if dq is None else _dense("dq", dq, q.dtype)
-    dk = torch.empty_like(k) if dk is None else _dense("dk", dk, q.dtype)
-    dv = torch.empty_like(v) if dv is None else _dense("dv", dv, q.dtype)
+    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape or lse.shape[0] != q.shape[0]:
+        raise ValueError(f"v {tuple(v.shape)}, out {tuple(out.shape)}, dout {tuple(dout.shape)} or lse "
+                         f"{tuple(lse.shape)} do not match q {tuple(q.shape)} / k {tuple(k.shape)}")
+    dev = _one_device(q=q, k=k, v=v, out=out, dout=dout, lse=lse, cu_q=cu_q, cu_k=cu_k, dq=dq, dk=dk, dv=dv,
+                      workspace=workspace)
+    dq = _out("dq", dq, q.shape, q.dtype, dev)
+    dk = _out("dk", dk, k.shape, q.dtype, dev)
+    dv = _out("dv", dv, v.shape, q.dtype, dev)
     code_dt = _dtype_code(q)
-    ws_bytes = bwd_varlen_workspace_bytes(B, hq, hkv, tq, tk, mq, mk, d, code_dt)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, bwd_varlen_workspace_bytes(B, hq, hkv, tq, tk, mq, mk, d, code_dt), dev)
     code = lib().flash_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
                                        _ptr(dk), _ptr(dv), _ptr(cu_q), _ptr(cu_k), B, hq, hkv, tq, tk, mq, mk, d,
                                        _default_scale(d, scale), int(bool(causal)), code_dt, _ptr(workspace),
@@ -255,11 +294,13 @@ def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool = Tru
     _dense("seq_lens", seq_lens, torch.int32, 1)
     B, Hq, Nq, d = q.shape
     num_blocks, Hkv, bs, _ = k_cache.shape
-    if v_cache.shape != k_cache.shape or block_table.shape[0] != B or seq_lens.shape[0] != B:
+    if v_cache.shape != k_cache.shape or k_cache.shape[3] != d or block_table.shape[0] != B or \
+            seq_lens.shape[0] != B:
         raise ValueError("cache, table or lengths do not match q")
-    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
-        _dense("lse", lse, torch.float32)
+    dev = _one_device(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, out=out,
+                      lse=lse)
+    out = _out("out", out, q.shape, q.dtype, dev)
+    lse = _out("lse", lse, (B, Hq, Nq), torch.float32, dev)
     code = lib().flash_attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                           _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, d, bs, block_table.shape[1], num_blocks,
                                           _default_scale(d, scale), int(bool(causal)), _dtype_code(q),
@@ -285,13 +326,10 @@ def fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal: bool =
     Hkv, Nk = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
         raise ValueError(f"k/v shapes {tuple(k.shape)}, {tuple(v.shape)} do not match q {tuple(q.shape)}")
-    out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else \
-        _dense("out", out, torch.bfloat16)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
-        _dense("lse", lse, torch.float32)
-    ws_bytes = fwd_fp8_workspace_bytes(B, Hkv, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    dev = _one_device(q=q, k=k, v=v, out=out, lse=lse, workspace=workspace)
+    out = _out("out", out, (B, Hq, Nq, d), torch.bfloat16, dev)
+    lse = _out("lse", lse, (B, Hq, Nq), torch.float32, dev)
+    workspace = _workspace(workspace, fwd_fp8_workspace_bytes(B, Hkv, Nk, d), dev)
     code = lib().flash_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                                     _default_scale(d, scale), float(q_descale), float(k_descale), float(v_descale),
                                     int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -321,14 +359,15 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_spl
     B, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_cache.shape
     max_blocks = block_table.shape[1]
-    out = torch.empty_like(q) if out is None else _dense("out", out, q.dtype)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    elif lse is not None:
-        _dense("lse", lse, torch.float32)
-    ws_bytes = decode_workspace_bytes(B, Hq, Hkv, d, max_blocks, bs, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if v_cache.shape != k_cache.shape or k_cache.shape[3] != d or block_table.shape[0] != B or \
+            seq_lens.shape[0] != B:
+        raise ValueError("cache, table or lengths do not match q")
+    dev = _one_device(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, out=out,
+                      lse=lse, workspace=workspace)
+    out = _out("out", out, q.shape, q.dtype, dev)
+    if lse is not None or want_lse:
+        lse = _out("lse", lse, (B, Hq), torch.float32, dev)
+    workspace = _workspace(workspace, decode_workspace_bytes(B, Hq, Hkv, d, max_blocks, bs, num_splits), dev)
     code = lib().flash_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                          _ptr(out), _ptr(lse), B, Hq, Hkv, d, bs, max_blocks, num_blocks,
                                          _default_scale(d, scale), int(num_splits), _dtype_code(q),
