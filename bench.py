@@ -22,17 +22,19 @@ single GPU.
 
 Helper modes produce the measured HBM traffic and counter figures that the
 roofline objects report (see `profiles/`):
-  python bench.py --profile-once
-      runs every kernel of the step and the decode once, plus a 1 GiB device
-      copy whose byte count calibrates the counters; run it under
-      `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE`;
+  python bench.py --profile-once [--profile-repeats R]
+      runs every kernel of the step, the decode and the FP8 forward once (or
+      R times), plus a 1 GiB device copy whose byte count calibrates the
+      counters; run it under `rocprofv3 --pmc FETCH_SIZE` and again under
+      `--pmc WRITE_SIZE`;
   python bench.py --traffic-from FETCH.csv WRITE.csv
       turns the two counter CSVs into profiles/traffic.json (bytes per launch,
       scaled by the copy's known bytes, tagged with the kernels' source hash)
       and profiles/hbm_traffic_mha_bf16_4k_decode_fp8.md;
   python bench.py --util-from COUNTERS.csv
       turns a counter CSV of --profile-once (MFMA busy cycles, GRBM active
-      cycles, LDS bank conflicts) into profiles/mfma_util.json.
+      cycles, LDS bank conflicts) into profiles/mfma_util.json, from the last
+      launch of each kernel.
 """
 
 from __future__ import annotations
@@ -313,28 +315,34 @@ def cpu_baseline(si, budget_s: float):
                       f"float64 numpy, {el:.1f} s; flops counted as for the GPU (visible pairs only)"}
 
 
-def profile_once(torch, fa, si):
-    """One launch of every kernel of the training step and of the decode, then
-    a 1 GiB device-to-device copy (counter calibration)."""
+def profile_once(torch, fa, si, repeats=1):
+    """``repeats`` launches of every kernel of the training step, of the decode
+    and of the FP8 forward, then a 1 GiB device-to-device copy (counter
+    calibration).  Counter readers take the last launch of each kernel (util)
+    or the mean over launches (bytes, which do not change between launches)."""
     w = si.WORKLOADS["mha_bf16_4k"]
     q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
-    o, lse = fa.fwd(q, k, v, causal=True)
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, fa.FA_BF16), dtype=torch.uint8,
                      device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, True)
-    fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, True)
-    fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, True)
+    for _ in range(repeats):
+        o, lse = fa.fwd(q, k, v, causal=True)
+        fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, True)
+        fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, True)
+        fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, True)
     torch.cuda.synchronize()
     del q, k, v, do, o, lse, ws, dq, dk, dv
     wd = si.WORKLOADS["decode_gqa_paged"]
     args = [t.to("cuda") for t in si.workload_decode_inputs(wd)]
-    fa.decode_paged(*args)
+    for _ in range(repeats):
+        fa.decode_paged(*args)
     torch.cuda.synchronize()
     del args
     wf = si.WORKLOADS["mha_fp8_4k"]
     q, k, v, desc = si.make_fp8_inputs(wf.B, wf.Hq, wf.Hkv, wf.Nq, wf.Nk, wf.d, wf.seed)
-    fa.fwd_fp8(q.to("cuda"), k.to("cuda"), v.to("cuda"), *desc, causal=True)
+    q, k, v = q.to("cuda"), k.to("cuda"), v.to("cuda")
+    for _ in range(repeats):
+        fa.fwd_fp8(q, k, v, *desc, causal=True)
     torch.cuda.synchronize()
     del q, k, v
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -381,13 +389,14 @@ def util_from(csv_path):
                                                        "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
             d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     rec = {"_definition": util_from.__doc__.split("\n", 1)[1].strip()}
-    for d in per.values():
-        # One launch per key: the first dispatch of its main kernel (the decode's
-        # split kernel, the FP8 forward rather than its V staging).
+    for _, d in sorted(per.items()):
+        # One launch per key: the last dispatch of its main kernel (the decode's
+        # split kernel, the FP8 forward rather than its V staging), the earlier
+        # ones being the warm-up.
         if "decode_reduce" in d["name"] or "fp8_vt" in d["name"]:
             continue
         key = next((k for pat, k in KERNEL_KEYS if pat in d["name"]), None)
-        if key is None or key in rec:
+        if key is None:
             continue
         c = d["c"]
         grbm = c["GRBM_GUI_ACTIVE"] / XCDS
@@ -459,11 +468,16 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # A burst of attention kernels on an idle MI355X runs about 7% slower for
+    # its first ~50 ms (5 warm-up steps: 642 TFLOP/s; 200: 686), so the
+    # default warm-up covers that before the timed steps.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-once", action="store_true", help="launch every kernel once (for rocprofv3 counters)")
+    ap.add_argument("--profile-repeats", type=int, default=1, metavar="R",
+                    help="with --profile-once: launch every kernel R times (the first ones warm the GPU up)")
     ap.add_argument("--util-from", metavar="COUNTER_CSV",
                     help="write profiles/mfma_util.json from a rocprofv3 counter CSV of --profile-once")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -489,7 +503,7 @@ def main(argv=None):
         return 1
     props = torch.cuda.get_device_properties(0)
     if args.profile_once:
-        profile_once(torch, fa, si)
+        profile_once(torch, fa, si, max(1, args.profile_repeats))
         return 0
 
     w, ms_step, per, wall = bench_training(torch, fa, si, args.steps, args.warmup)
