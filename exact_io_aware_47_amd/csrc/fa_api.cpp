@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per tensor, keeps 32-bit element offsets valid
 constexpr int kCUs = 256;                        // MI355X compute units (sizes the automatic split count)
+constexpr int kMaxDecodeSplits = 1 << 16;        // explicit decode split counts above this are refused
 
 int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 bool dtype_ok(int dtype) { return dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16; }
@@ -281,7 +282,7 @@ int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int blo
 size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq, int block_size,
                                          int num_splits) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !headdim_ok(d) || max_blocks_per_seq <= 0 ||
-      block_size != 16 || num_splits < 0)
+      block_size != 16 || num_splits < 0 || num_splits > kMaxDecodeSplits)
     return 0;
   const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
   return (size_t)B * Hq * splits * (d + 4) * sizeof(float);  // [O (d), m, l, 2 pad] per split
@@ -298,7 +299,12 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
   if (!headdim_ok(d)) return FA_ERR_HEADDIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   if (block_size != 16) return FA_ERR_BLOCKSIZE;
-  if ((int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)B * Hq * d >= kMaxElems) return FA_ERR_SHAPE;
+  // The split kernel's grid is (work-groups per (sequence, K/V head), B * Hkv):
+  // its second dimension stays within 65535, and the split count within
+  // kMaxDecodeSplits so that the first cannot overflow.
+  if ((int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)B * Hq * d >= kMaxElems ||
+      (int64_t)B * Hkv > 65535 || num_splits > kMaxDecodeSplits)
+    return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
   if (!workspace ||

@@ -201,7 +201,8 @@ int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int blo
  * Bytes of device workspace flash_attn_decode_paged needs for the given
  * split count (0 = automatic, resolved as above): per (sequence, query head,
  * split) a record of d + 4 float32 values (the partial output, its running
- * max and sum, two pad words).  Returns 0 for invalid sizes.
+ * max and sum, two pad words).  Returns 0 for invalid sizes (num_splits
+ * outside [0, 65536] included).
  */
 size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq,
                                          int block_size, int num_splits);
@@ -225,8 +226,10 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  * (no mask).  Each split runs an online softmax over its share of the pages;
  * a second kernel merges the splits' (max, sum, output) partials.
  * block_size must be 16.  dtype must be FA_F16 or FA_BF16 (the float32 KV
- * cache is not supported: FA_ERR_DTYPE).  num_splits >= 0 (0 = automatic);
- * results depend on the split count only through float32 rounding order.
+ * cache is not supported: FA_ERR_DTYPE).  0 <= num_splits <= 65536 (0 =
+ * automatic); results depend on the split count only through float32
+ * rounding order.  B * Hkv <= 65535 (the split kernel's grid), else
+ * FA_ERR_SHAPE.
  * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
  * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
  * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_LAUNCH.

@@ -163,6 +163,8 @@ def dec(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128
     (dict(B=0), SHAPE), (dict(max_blocks=0), SHAPE), (dict(nblocks=0), SHAPE), (dict(splits=-1), SHAPE),
     (dict(d=80), HEADDIM), (dict(Hq=8, Hkv=3), GQA), (dict(bs=32), BLOCKSIZE), (dict(bs=8), BLOCKSIZE),
     (dict(scale=INF), SCALE),
+    (dict(B=65536, Hkv=1, Hq=1), SHAPE), (dict(B=16384, Hkv=4, Hq=4), SHAPE),   # the split grid's second dimension
+    (dict(splits=(1 << 16) + 1), SHAPE), (dict(splits=2 ** 31 - 1), SHAPE),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
     (dict(), ALIGN), (dict(lse=None), ALIGN),
 ])
@@ -213,6 +215,8 @@ def test_workspace_queries(L):
     assert L.flash_attn_bwd_varlen_workspace_bytes(16, 16, 16, 35457, 35457, 4000, 4000, 128, BF16) == 2 * 16 * 35457 * 4
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 0, 10, 0, 10, 64, F16) == 0
     assert L.flash_attn_bwd_varlen_workspace_bytes(2, 4, 2, 10, 10, 11, 10, 64, F16) == 0
+    assert L.flash_attn_decode_workspace_bytes(2, 8, 2, 128, 4, 16, 1 << 16) == 2 * 8 * (1 << 16) * 132 * 4
+    assert L.flash_attn_decode_workspace_bytes(2, 8, 2, 128, 4, 16, (1 << 16) + 1) == 0
     # FP8: V staged transposed in 64-key tiles, one byte per element.
     assert L.flash_attn_fwd_fp8_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 128
     assert L.flash_attn_fwd_fp8_workspace_bytes(1, 2, 200, 64) == 1 * 2 * 256 * 64
