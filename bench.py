@@ -376,7 +376,7 @@ def _counter_sums(path, counter):
 SIMDS, XCDS = 1024, 8  # MI355X: 256 compute units x 4 SIMDs, 8 XCDs
 
 
-def util_from(csv_path):
+def util_from(csv_path, out_dir=None):
     """profiles/mfma_util.json from one rocprofv3 counter CSV of --profile-once:
     MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x SIMDs)
     (rocprofv3's MfmaUtil), clock = GRBM_GUI_ACTIVE per XCD / duration, LDS bank
@@ -405,12 +405,15 @@ def util_from(csv_path):
                     "lds_bank_conflicts_per_access": round(
                         c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"]), 4),
                     "us": round(d["us"], 2), "source_hash": source_hash(*KERNEL_SOURCES[key])}
-    with open(os.path.join(ROOT, "profiles", "mfma_util.json"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "mfma_util.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+    return rec
 
 
-def traffic_from(fetch_csv, write_csv):
+def traffic_from(fetch_csv, write_csv, out_dir=None):
     fetch, write = _counter_sums(fetch_csv, "FETCH_SIZE"), _counter_sums(write_csv, "WRITE_SIZE")
     def per_key(rows):
         acc, copy = {}, []
@@ -437,8 +440,9 @@ def traffic_from(fetch_csv, write_csv):
         rec[key] = {"fetch_bytes": round(fbytes), "write_bytes": round(wbytes),
                     "hbm_bytes_per_launch": round(fbytes + wbytes),
                     "source_hash": source_hash(*KERNEL_SOURCES[key])}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     # Text summary next to it.
     w = None
@@ -459,9 +463,10 @@ def traffic_from(fetch_csv, write_csv):
         if key in rec:
             r = rec[key]
             lines.append(f"| {key} | {r['fetch_bytes']:,} | {r['write_bytes']:,} | {r['hbm_bytes_per_launch']:,} |")
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic_mha_bf16_4k_decode_fp8.md"), "w") as f:
+    with open(os.path.join(out_dir, "hbm_traffic_mha_bf16_4k_decode_fp8.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
+    return rec
 
 
 def main(argv=None):

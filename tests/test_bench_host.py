@@ -35,3 +35,53 @@ def test_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def _counter_csv(path, rows):
+    """A rocprofv3-style counter CSV: rows of (dispatch, kernel, counter, value, start, end)."""
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_util_from_reads_the_last_launch_of_each_kernel(tmp_path):
+    fwd = "fa::fwd_kernel<bf16>"
+    rows = []
+    # Two launches of the forward: 1000 ns at half MFMA busy, then 500 ns fully busy.
+    # GRBM_GUI_ACTIVE sums 8 XCDs; MFMA busy cycles sum 1024 SIMDs.
+    for disp, start, end, grbm_xcd, busy in ((1, 0, 1000, 2000, 0.5), (2, 2000, 2500, 1200, 1.0)):
+        rows += [(disp, fwd, "GRBM_GUI_ACTIVE", 8 * grbm_xcd, start, end),
+                 (disp, fwd, "SQ_VALU_MFMA_BUSY_CYCLES", busy * grbm_xcd * 1024, start, end),
+                 (disp, fwd, "SQ_LDS_BANK_CONFLICT", 10, start, end),
+                 (disp, fwd, "SQ_LDS_IDX_ACTIVE", 110, start, end)]
+    _counter_csv(tmp_path / "c.csv", rows)
+    rec = bench.util_from(str(tmp_path / "c.csv"), out_dir=str(tmp_path))
+    assert rec["fwd"]["mfma_busy"] == 1.0
+    assert rec["fwd"]["clock_ghz"] == 2.4                    # 1200 cycles in 500 ns
+    assert rec["fwd"]["lds_bank_conflicts_per_access"] == 0.1
+    assert rec["fwd"]["us"] == 0.5
+    assert os.path.exists(tmp_path / "mfma_util.json")
+
+
+def test_traffic_from_scales_by_the_calibration_copy(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = bench.COPY_BYTES // 1024
+    # The counters read the copy at half its true bytes; the decode's split and
+    # reduce kernels are summed per launch, averaged over launches.
+    fetch = [(1, copy, "FETCH_SIZE", gib_kib / 2, 0, 1),
+             (2, "decode_split_kernel<bf16>", "FETCH_SIZE", 100, 0, 1),
+             (3, "decode_reduce_kernel<bf16>", "FETCH_SIZE", 10, 0, 1),
+             (4, "decode_split_kernel<bf16>", "FETCH_SIZE", 300, 0, 1)]
+    write = [(1, copy, "WRITE_SIZE", gib_kib, 0, 1),
+             (2, "decode_split_kernel<bf16>", "WRITE_SIZE", 4, 0, 1),
+             (3, "decode_reduce_kernel<bf16>", "WRITE_SIZE", 1, 0, 1)]
+    _counter_csv(tmp_path / "f.csv", fetch)
+    _counter_csv(tmp_path / "w.csv", write)
+    rec = bench.traffic_from(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out_dir=str(tmp_path))
+    assert rec["_calibration"]["fetch_factor"] == 2.0 and rec["_calibration"]["write_factor"] == 1.0
+    assert rec["decode"]["fetch_bytes"] == (200 + 10) * 1024 * 2
+    assert rec["decode"]["write_bytes"] == (4 + 1) * 1024
+    assert os.path.exists(tmp_path / "traffic.json") and os.path.exists(tmp_path / "hbm_traffic_mha_bf16_4k_decode_fp8.md")
