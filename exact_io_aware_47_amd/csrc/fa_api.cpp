@@ -10,7 +10,6 @@
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per tensor, keeps 32-bit element offsets valid
-constexpr int kCUs = 256;                        // MI355X compute units (sizes the automatic split count)
 constexpr int kMaxDecodeSplits = 1 << 16;        // explicit decode split counts above this are refused
 
 int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
@@ -88,6 +87,7 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
   a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
+  a.cus = fa::device_cu_count();
   return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -105,6 +105,7 @@ int flash_attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, 
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = max_seqlen_q; a.Nk = max_seqlen_k; a.d = d;
   a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.tot_q = total_q; a.tot_k = total_k;
+  a.cus = fa::device_cu_count();
   return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -231,6 +232,7 @@ int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_c
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = max_blocks_per_seq * block_size; a.d = d;
   a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
   a.block_table = block_table; a.seq_lens = seq_lens; a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks;
+  a.cus = fa::device_cu_count();
   return launch_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -268,11 +270,11 @@ int flash_attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, flo
 
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size) {
   if (B <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || block_size != 16) return 0;
-  // Aim for 4 splits (waves) per compute unit, with at least 4 pages per
-  // split: measured on the 32768-token decode, 16 splits per sequence and
-  // K/V head beat 8, 32 and 64.
+  // Aim for 4 splits (waves) per compute unit of the current device, with at
+  // least 4 pages per split: measured on the 32768-token decode (256 compute
+  // units), 16 splits per sequence and K/V head beat 8, 32 and 64.
   const int64_t units = (int64_t)B * Hkv;
-  int64_t splits = (4 * kCUs + units - 1) / units;
+  int64_t splits = (4 * (int64_t)fa::device_cu_count() + units - 1) / units;
   const int64_t max_splits = max_blocks_per_seq / 4 > 0 ? max_blocks_per_seq / 4 : 1;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -302,8 +304,8 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
   // The split kernel's grid is (work-groups per (sequence, K/V head), B * Hkv):
   // its second dimension stays within 65535, and the split count within
   // kMaxDecodeSplits so that the first cannot overflow.
-  if ((int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)B * Hq * d >= kMaxElems ||
-      (int64_t)B * Hkv > 65535 || num_splits > kMaxDecodeSplits)
+  if ((int64_t)B * max_blocks_per_seq >= kMaxElems || (int64_t)max_blocks_per_seq * block_size >= kMaxElems ||
+      (int64_t)B * Hq * d >= kMaxElems || (int64_t)B * Hkv > 65535 || num_splits > kMaxDecodeSplits)
     return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);

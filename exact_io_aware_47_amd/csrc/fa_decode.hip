@@ -99,7 +99,8 @@ void decode_split_kernel(SplitParams p, const int* __restrict__ block_table,
   const bool q_ok = qi < g;
   const int hq = hkv * g + qi;
 
-  const int seq_len = seq_lens[b];
+  // Tokens of the sequence, clamped to what its table row can address.
+  const int seq_len = min(max(seq_lens[b], 0), p.max_blocks * C::kPage);
   const int n_pages = (seq_len + C::kPage - 1) / C::kPage;
   const int pg0 = (int)((int64_t)n_pages * split / p.splits);
   const int pg1 = (int)((int64_t)n_pages * (split + 1) / p.splits);

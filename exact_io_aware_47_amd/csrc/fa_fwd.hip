@@ -477,13 +477,12 @@ hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
   return a.causal ? launch_typed<T, D, true, false, W>(a, s) : launch_typed<T, D, false, false, W>(a, s);
 }
 
-constexpr int kCUs = 256;  // MI355X compute units
-
-// 8-wave work-groups unless that grid gives fewer than two per compute unit.
+// 8-wave work-groups unless that grid gives fewer than two per compute unit
+// of the device.
 template <typename T, int D>
 hipError_t launch_waves(const FwdArgs& a, hipStream_t s) {
   const int64_t grid8 = (int64_t)((a.Nq + FwdCfg<T, D, 8>::kBR - 1) / FwdCfg<T, D, 8>::kBR) * a.B * a.Hq;
-  return grid8 < 2 * kCUs ? launch_mask<T, D, 4>(a, s) : launch_mask<T, D, 8>(a, s);
+  return grid8 < 2 * (int64_t)a.cus ? launch_mask<T, D, 4>(a, s) : launch_mask<T, D, 8>(a, s);
 }
 
 template <typename T>

@@ -6,6 +6,14 @@
 
 namespace fa {
 
+// Compute units of a whole MI355X.  Launch heuristics use the current
+// device's count (device_cu_count); this is its value when no device answers.
+constexpr int kFullChipCUs = 256;
+
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount),
+// or kFullChipCUs if the query fails.  One HIP runtime query per call.
+int device_cu_count();
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -27,6 +35,8 @@ struct FwdArgs {
   const int* block_table = nullptr;
   const int* seq_lens = nullptr;
   int max_blocks = 0, num_blocks = 0;
+  // Compute units of the device the launch runs on (sizes the work-groups).
+  int cus = kFullChipCUs;
 };
 
 struct BwdArgs {

@@ -192,17 +192,22 @@ int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const voi
 
 /*
  * Number of KV splits the decode uses for num_splits = 0 (automatic): about
- * four splits (one per wave) per compute unit of the 256, with at least 4
- * pages per split.  Pure host arithmetic, no HIP call.
+ * four splits (one per wave) per compute unit of the current device (256 on
+ * a whole MI355X; 256 is also assumed when the device query fails), with at
+ * least 4 pages per split.  Its only HIP call is that device query, made
+ * after the arguments are checked; invalid sizes return 0.
  */
 int flash_attn_decode_num_splits(int B, int Hkv, int max_blocks_per_seq, int block_size);
 
 /*
  * Bytes of device workspace flash_attn_decode_paged needs for the given
- * split count (0 = automatic, resolved as above): per (sequence, query head,
- * split) a record of d + 4 float32 values (the partial output, its running
- * max and sum, two pad words).  Returns 0 for invalid sizes (num_splits
- * outside [0, 65536] included).
+ * split count (0 = automatic, resolved as above on the current device, so
+ * query it with the device current that the decode will run on): per
+ * (sequence, query head, split) a record of d + 4 float32 values (the
+ * partial output, its running max and sum, two pad words).  Besides the
+ * split count itself, the automatic count needs Hkv, max_blocks_per_seq and
+ * block_size, which is why they are arguments.  Returns 0 for invalid sizes
+ * (num_splits outside [0, 65536] included).
  */
 size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_blocks_per_seq,
                                          int block_size, int num_splits);
@@ -217,10 +222,11 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  *               [0, num_blocks); entries past a sequence's last page are
  *               never read.  An id outside [0, num_blocks) is read as a page
  *               of zeros (it cannot fault, but the result is meaningless).
- *   seq_lens    [B] int32 device array, 0 <= seq_lens[b] <=
- *               max_blocks_per_seq * block_size (tokens of sequence b; the
- *               tail of its last page is ignored).  A length of 0 gives O = 0
- *               and LSE = -inf.
+ *   seq_lens    [B] int32 device array: tokens of sequence b (the tail of
+ *               its last page is ignored).  Values outside [0,
+ *               max_blocks_per_seq * block_size] are clamped to that range,
+ *               so no length reads past the sequence's table row.  A length
+ *               of 0 gives O = 0 and LSE = -inf.
  *   O   [B, Hq, d] dtype;  LSE [B, Hq] float32, or NULL if not wanted.
  * The query is the sequence's last position, so it sees every cached token
  * (no mask).  Each split runs an online softmax over its share of the pages;
@@ -228,8 +234,8 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
  * block_size must be 16.  dtype must be FA_F16 or FA_BF16 (the float32 KV
  * cache is not supported: FA_ERR_DTYPE).  0 <= num_splits <= 65536 (0 =
  * automatic); results depend on the split count only through float32
- * rounding order.  B * Hkv <= 65535 (the split kernel's grid), else
- * FA_ERR_SHAPE.
+ * rounding order.  B * Hkv <= 65535 (the split kernel's grid) and
+ * max_blocks_per_seq * block_size below 2^31, else FA_ERR_SHAPE.
  * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
  * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
  * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_LAUNCH.

@@ -3,7 +3,12 @@ and rejects bad arguments with the documented codes before any HIP call.
 
 Fake device pointers here are deliberately 8-byte (not 16-byte) aligned, so a
 call whose other arguments were valid would still stop at FA_ERR_ALIGN: no
-test in this file can reach a kernel launch.
+test in this file can reach a kernel launch of the real library.
+
+With FA_ABI_STUB_LIB naming a build of the ABI layer whose launchers are
+host-only stubs (the sanitizer build of tests/test_abi_asan.py), the same
+tests run against that build, and the tests marked ``stub_only`` also make
+valid calls with aligned fake pointers that reach the (stub) launchers.
 """
 
 from __future__ import annotations
@@ -35,9 +40,21 @@ def fa():
     return pkg
 
 
+STUB_LIB = os.environ.get("FA_ABI_STUB_LIB")
+stub_only = pytest.mark.skipif(not STUB_LIB, reason="needs the host-only stub build (FA_ABI_STUB_LIB)")
+
+
 @pytest.fixture(scope="module")
 def L(fa):
-    return fa.lib()
+    if not STUB_LIB:
+        return fa.lib()
+    from exact_io_aware_47_amd import _lib
+    handle = ctypes.CDLL(STUB_LIB)
+    for name, (res, args) in _lib.SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype, fn.argtypes = res, args
+    handle.fa_stub_launch_count.restype, handle.fa_stub_launch_count.argtypes = ctypes.c_int, []
+    return handle
 
 
 def declared_functions():
@@ -164,6 +181,7 @@ def dec(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128
     (dict(d=80), HEADDIM), (dict(Hq=8, Hkv=3), GQA), (dict(bs=32), BLOCKSIZE), (dict(bs=8), BLOCKSIZE),
     (dict(scale=INF), SCALE),
     (dict(B=65536, Hkv=1, Hq=1), SHAPE), (dict(B=16384, Hkv=4, Hq=4), SHAPE),   # the split grid's second dimension
+    (dict(B=1, max_blocks=1 << 27), SHAPE),   # max_blocks * 16 tokens reaches 2^31
     (dict(splits=(1 << 16) + 1), SHAPE), (dict(splits=2 ** 31 - 1), SHAPE),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
     (dict(), ALIGN), (dict(lse=None), ALIGN),
@@ -240,3 +258,51 @@ def test_binding_refuses_host_tensors(fa):
 def test_binding_maps_error_codes(fa, L):
     err = fa.FlashAttnError(GQA, "flash_attn_fwd")
     assert err.code == GQA and "FA_ERR_GQA" in str(err)
+
+
+A = 0x10000  # fake, 16-byte aligned device pointer (stub build only: nothing dereferences it)
+
+
+@stub_only
+def test_valid_calls_reach_the_launchers(L):
+    """Every entry point, with valid arguments, passes validation and calls
+    its launcher once (stub build: the launchers only count)."""
+    big = 1 << 40
+    calls = [
+        lambda: fwd(L, q=A, k=A, v=A, o=A, lse=A),
+        lambda: fwd(L, q=A, k=A, v=A, o=A, lse=A, dtype=F32, causal=1, Nq=300, Nk=77, d=128),
+        lambda: L.flash_attn_bwd(A, A, A, A, A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
+        lambda: L.flash_attn_bwd_preprocess(A, A, A, 1, 4, 100, 64, BF16, A, big, None),
+        lambda: L.flash_attn_bwd_dkdv(A, A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
+        lambda: L.flash_attn_bwd_dq(A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
+        lambda: fwd_vl(L, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A),
+        lambda: fwd_vl(L, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, tq=0, mq=0, tk=0, mk=0),
+        lambda: L.flash_attn_bwd_varlen(A, A, A, A, A, A, A, A, A, A, A, 3, 4, 2, 300, 300, 200, 200, 64, 0.1, 1,
+                                        F16, A, big, None),
+        lambda: pre(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A),
+        lambda: fp8(L, q=A, k=A, v=A, o=A, lse=A, ws=A, ws_bytes=big),
+        lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=big),
+        lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=None, ws=A, ws_bytes=big, splits=1 << 16),
+        lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=big, B=65535, Hq=1, Hkv=1),
+    ]
+    for i, call in enumerate(calls):
+        before = L.fa_stub_launch_count()
+        assert call() == OK, f"call {i}"
+        assert L.fa_stub_launch_count() == before + 1, f"call {i} did not reach its launcher"
+
+
+@stub_only
+def test_workspace_boundaries_exact(L):
+    """A workspace of exactly the queried size is accepted, one byte less is not."""
+    need = L.flash_attn_bwd_workspace_bytes(2, 8, 4, 333, 333, 128, BF16)
+    args = (2, 8, 4, 333, 333, 128, 0.1, 1, BF16)
+    assert L.flash_attn_bwd(A, A, A, A, A, A, A, A, A, *args, A, need, None) == OK
+    assert L.flash_attn_bwd(A, A, A, A, A, A, A, A, A, *args, A, need - 1, None) == WORKSPACE
+    need = L.flash_attn_decode_workspace_bytes(8, 32, 8, 128, 2048, 16, 0)
+    assert dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=need, B=8, Hq=32, Hkv=8,
+               max_blocks=2048, nblocks=16384) == OK
+    assert dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=need - 1, B=8, Hq=32, Hkv=8,
+               max_blocks=2048, nblocks=16384) == WORKSPACE
+    need = L.flash_attn_fwd_fp8_workspace_bytes(1, 2, 200, 128)
+    assert fp8(L, q=A, k=A, v=A, o=A, lse=A, ws=A, ws_bytes=need) == OK
+    assert fp8(L, q=A, k=A, v=A, o=A, lse=A, ws=A, ws_bytes=need - 1) == WORKSPACE

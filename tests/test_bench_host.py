@@ -66,6 +66,20 @@ def test_util_from_reads_the_last_launch_of_each_kernel(tmp_path):
     assert os.path.exists(tmp_path / "mfma_util.json")
 
 
+def test_util_from_drops_counters_of_launches_shorter_than_the_window(tmp_path):
+    """GRBM cycles beyond duration x 2.4 GHz mean the counter window outlasted
+    the launch: busy fraction and clock are then not reported."""
+    prep = "fa::bwd_prep_kernel<bf16>"
+    rows = [(1, prep, "GRBM_GUI_ACTIVE", 8 * 3934, 0, 1000),   # 3.934 GHz over 1 us: impossible
+            (1, prep, "SQ_VALU_MFMA_BUSY_CYCLES", 0, 0, 1000),
+            (1, prep, "SQ_LDS_BANK_CONFLICT", 0, 0, 1000),
+            (1, prep, "SQ_LDS_IDX_ACTIVE", 10, 0, 1000)]
+    _counter_csv(tmp_path / "c.csv", rows)
+    rec = bench.util_from(str(tmp_path / "c.csv"), out_dir=str(tmp_path))
+    assert rec["prep"]["mfma_busy"] is None and rec["prep"]["clock_ghz"] is None
+    assert rec["prep"]["lds_bank_conflicts_per_access"] == 0.0
+
+
 def test_traffic_from_scales_by_the_calibration_copy(tmp_path):
     copy = "__amd_rocclr_copyBuffer"
     gib_kib = bench.COPY_BYTES // 1024

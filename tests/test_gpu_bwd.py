@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -57,6 +58,12 @@ CASES = [
     (1, 2, 2, 64, 1000, 128, "bf16", True),
     (2, 4, 2, 700, 256, 64, "bf16", True),
     (1, 3, 1, 200, 700, 128, "f16", True),
+    # bfloat16 at d = 32
+    (2, 4, 4, 333, 333, 32, "bf16", True),
+    (1, 3, 1, 200, 517, 32, "bf16", False),
+    # many heads of short sequences (the forward runs 8-wave work-groups)
+    (2, 256, 64, 257, 300, 64, "bf16", True),
+    (2, 128, 128, 300, 257, 128, "f16", False),
 ]
 
 
@@ -87,13 +94,33 @@ def test_bwd_workload_mha_f16(causal):
     check_grads(q, k, v, do, causal, "f16")
 
 
-def _sampled_heads(w, heads):
+def _oracle_bwd_rows(q, k, v, do, scale, causal, chunk):
+    """The oracle's gradients of one (batch, head), taking the query rows in
+    chunks: dQ rows come from their own chunk, dK and dV sum the chunks'
+    contributions (each row's terms depend on that row alone)."""
+    nq = q.shape[2]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for r0 in range(0, nq, chunk):
+        rows = np.arange(r0, min(r0 + chunk, nq))
+        gq, gk, gv = orc.attention_bwd(q[:, :, rows], k, v, do[:, :, rows], scale, causal, row_ids=rows, nq_total=nq)
+        dq[:, :, rows] = gq
+        dk += gk
+        dv += gv
+    return dq, dk, dv
+
+
+def _heads_check(w, heads, chunk=None):
     q, k, v, do = si.workload_attention_inputs(w)
     dq, dk, dv = run_fwd_bwd(q, k, v, do, True)
     large = w.qk_mult != 1.0
     for b, h in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv = orc.attention_bwd(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]), w.scale, True)
+        if chunk is None:
+            rq, rk, rv = orc.attention_bwd(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]), w.scale, True)
+        else:
+            rq, rk, rv = _oracle_bwd_rows(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]), w.scale, True, chunk)
         assert_close(f"dQ[{b},{h}]", f64(dq[sl]), rq, w.dtype, "grad", large)
         assert_close(f"dK[{b},{h}]", f64(dk[sl]), rk, w.dtype, "grad", large)
         assert_close(f"dV[{b},{h}]", f64(dv[sl]), rv, w.dtype, "grad", large)
@@ -101,27 +128,31 @@ def _sampled_heads(w, heads):
 
 
 def test_bwd_workload_mha_bf16_4k():
-    _sampled_heads(si.WORKLOADS["mha_bf16_4k"], [(0, 0), (1, 13)])
+    """The benchmarked launch, compared in full (every head)."""
+    w = si.WORKLOADS["mha_bf16_4k"]
+    _heads_check(w, [(b, h) for b in range(w.B) for h in range(w.Hq)])
 
 
 def test_bwd_workload_gqa_bf16_4k():
     """Grouped heads at the training shape: dK/dV of one K/V head are the sum
-    over its four query heads, so the oracle takes the whole group."""
+    over its four query heads, so the oracle takes whole groups (three of
+    them, the last included)."""
     w = si.WORKLOADS["gqa_bf16_4k"]
     q, k, v, do = si.workload_attention_inputs(w)
     dq, dk, dv = run_fwd_bwd(q, k, v, do, True)
     g = w.Hq // w.Hkv
-    b, hkv = 1, 5
-    qs = (slice(b, b + 1), slice(hkv * g, (hkv + 1) * g))
-    ks = (slice(b, b + 1), slice(hkv, hkv + 1))
-    rq, rk, rv = orc.attention_bwd(f64(q[qs]), f64(k[ks]), f64(v[ks]), f64(do[qs]), w.scale, True)
-    assert_close(f"dQ[{b},group {hkv}]", f64(dq[qs]), rq, w.dtype, "grad")
-    assert_close(f"dK[{b},{hkv}]", f64(dk[ks]), rk, w.dtype, "grad")
-    assert_close(f"dV[{b},{hkv}]", f64(dv[ks]), rv, w.dtype, "grad")
+    for b, hkv in ((0, 0), (1, 5), (1, w.Hkv - 1)):
+        qs = (slice(b, b + 1), slice(hkv * g, (hkv + 1) * g))
+        ks = (slice(b, b + 1), slice(hkv, hkv + 1))
+        rq, rk, rv = orc.attention_bwd(f64(q[qs]), f64(k[ks]), f64(v[ks]), f64(do[qs]), w.scale, True)
+        assert_close(f"dQ[{b},group {hkv}]", f64(dq[qs]), rq, w.dtype, "grad")
+        assert_close(f"dK[{b},{hkv}]", f64(dk[ks]), rk, w.dtype, "grad")
+        assert_close(f"dV[{b},{hkv}]", f64(dv[ks]), rv, w.dtype, "grad")
 
 
 def test_bwd_workload_mha_bf16_16k():
-    dq, dk, dv = _sampled_heads(si.WORKLOADS["mha_bf16_16k"], [(0, 5)])
+    """Two whole heads, the last included (oracle rows in chunks of 2048)."""
+    dq, dk, dv = _heads_check(si.WORKLOADS["mha_bf16_16k"], [(0, 5), (0, 15)], chunk=2048)
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
 

@@ -67,6 +67,22 @@ def test_decode_matches_oracle(B, Hq, Hkv, lens, d, dtype, splits):
             assert (o[b] == 0).all() and torch.isneginf(lse[b]).all()
 
 
+def test_decode_clamps_out_of_range_lengths():
+    """A length beyond the table row's reach (the last sequence included) is
+    clamped to max_blocks * 16, a negative one to 0: compared with the oracle
+    on the clamped lengths."""
+    q, kc, vc, table, sl = si.make_decode_inputs(3, 8, 2, [100, 40, 70], 128, "bf16", seed=3101, extra_blocks=3)
+    max_blocks = table.shape[1]
+    for lens in ([100, -5, 2 ** 31 - 1], [-1, 100000, 7]):
+        given = torch.tensor(lens, dtype=torch.int32)
+        clamped = given.clamp(0, max_blocks * 16)
+        sc = 1.0 / math.sqrt(128)
+        o, lse = run_decode(q, kc, vc, table, given, sc)
+        ro, rl = oracle_decode(q, kc, vc, table, clamped, sc)
+        assert_close("O", f64(o), ro, "bf16", "o")
+        assert_close("LSE", f64(lse), rl, "bf16", "lse")
+
+
 def test_decode_ignores_garbage_past_sequence_end():
     """Cache slots past each sequence's length hold NaN; they must not leak."""
     B, Hq, Hkv, d = 3, 8, 2, 128

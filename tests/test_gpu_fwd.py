@@ -1,9 +1,9 @@
 """GPU parity of the forward kernel against the float64 oracle.
 
-Small and ragged shapes are compared element by element in full; the two
-large training workloads run at full size on the GPU (the launch the
-benchmark times) and are compared on sampled heads / rows that the oracle
-evaluates one by one.
+Small and ragged shapes are compared element by element in full.  The large
+workloads run at full size on the GPU (the launch the benchmark times): the
+4k training shapes are compared in full, the 16k shape on every row of four
+heads (the oracle takes the rows in chunks).
 """
 
 from __future__ import annotations
@@ -48,6 +48,9 @@ CASES = [
     (1, 2, 2, 64, 64, 128, "f16", True),
     (1, 1, 1, 4096, 77, 64, "bf16", False),
     (3, 6, 3, 190, 190, 128, "f16", False),
+    # bfloat16 at d = 32 on the dense path
+    (2, 4, 4, 333, 333, 32, "bf16", True),
+    (1, 3, 1, 200, 517, 32, "bf16", False),
 ]
 
 
@@ -112,23 +115,54 @@ def _sampled_heads_check(w, heads, row_ids=None):
     return o, lse
 
 
+def _all_heads(w):
+    return [(b, h) for b in range(w.B) for h in range(w.Hq)]
+
+
 def test_fwd_workload_mha_bf16_4k():
+    """The benchmarked launch, compared in full (every head, every row)."""
     w = si.WORKLOADS["mha_bf16_4k"]
-    _sampled_heads_check(w, [(0, 0), (1, 15), (0, 9)])
+    _sampled_heads_check(w, _all_heads(w))
 
 
 def test_fwd_workload_gqa_bf16_4k():
     w = si.WORKLOADS["gqa_bf16_4k"]
-    _sampled_heads_check(w, [(0, 0), (1, 22)])
+    _sampled_heads_check(w, _all_heads(w))
 
 
 def test_fwd_workload_mha_bf16_16k():
+    """Every row of four heads, the last included; the oracle takes the rows
+    in chunks of 2048 to bound host memory."""
     w = si.WORKLOADS["mha_bf16_16k"]
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(w.Nq - 40, w.Nq),
-                                     rng.choice(w.Nq, 200, replace=False)]))
-    o, lse = _sampled_heads_check(w, [(0, 0), (0, 11)], row_ids=rows)
+    q, k, v, _ = si.workload_attention_inputs(w)
+    o, lse = run_fwd(q, k, v, True)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    g = w.Hq // w.Hkv
+    for b, h in ((0, 0), (0, 5), (0, 11), (0, 15)):
+        kh, vh = f64(k[b:b + 1, h // g:h // g + 1]), f64(v[b:b + 1, h // g:h // g + 1])
+        for r0 in range(0, w.Nq, 2048):
+            rows = np.arange(r0, min(r0 + 2048, w.Nq))
+            o_ref, lse_ref = orc.attention_fwd(f64(q[b:b + 1, h:h + 1, rows]), kh, vh, w.scale, True,
+                                               row_ids=rows, nq_total=w.Nq)
+            assert_close(f"O[{b},{h}] rows {r0}..", f64(o[b:b + 1, h:h + 1, rows]), o_ref, w.dtype, "o")
+            assert_close(f"LSE[{b},{h}] rows {r0}..", f64(lse[b:b + 1, h:h + 1, rows]), lse_ref, w.dtype, "lse")
+
+
+# Many heads of short sequences: B * Hq * ceil(Nq / 256) >= 2 * 256, so these
+# run the 8-wave (256-row) work-groups that the long workloads use, in every
+# dtype and head size, with Nq != Nk both ways and grouped heads.
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_fwd_eight_wave_grids(dtype, d):
+    for (B, Hq, Hkv, Nq, Nk) in ((2, 256, 64, 257, 300), (2, 256, 256, 300, 257)):
+        assert B * Hq * -(-Nq // 256) >= 512
+        q, k, v, _ = si.make_attention_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed=9000 + d + Nq)
+        for causal in (True, False):
+            print(f"8-wave fwd {dtype} d={d} B={B} H={Hq}x{Hkv} N={Nq}x{Nk} causal={causal}", flush=True)
+            o, lse = run_fwd(q, k, v, causal)
+            o_ref, lse_ref = orc.attention_fwd(f64(q), f64(k), f64(v), scale_for(d), causal)
+            assert_close("O", f64(o), o_ref, dtype, "o")
+            assert_close("LSE", f64(lse), lse_ref, dtype, "lse")
 
 
 def test_fwd_bitwise_repeatable():

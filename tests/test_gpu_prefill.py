@@ -44,6 +44,7 @@ CASES = [
     (2, 2, 2, 33, [64, 90], 128, "f32", False),
     (1, 4, 4, 300, [1200], 64, "bf16", True),
     (2, 4, 1, 1, [500, 31], 128, "bf16", True),        # one query: the decode's case
+    (2, 256, 64, 257, [300, 280], 64, "bf16", True),   # 8-wave work-groups (B * Hq * 2 tiles >= 512)
 ]
 
 
@@ -54,6 +55,22 @@ def test_prefill_matches_oracle(B, Hq, Hkv, Nq, lens, d, dtype, causal):
     print(f"prefill case B={B} H={Hq}x{Hkv} Nq={Nq} lens={lens} d={d} {dtype} causal={causal}", flush=True)
     inputs = si.make_prefill_inputs(B, Hq, Hkv, Nq, lens, d, dtype, seed=6000 + Nq + sum(lens) + d, extra_blocks=5)
     check(*inputs, causal, dtype)
+
+
+def test_prefill_clamps_out_of_range_lengths():
+    """Lengths beyond the table row's reach (the last sequence included) are
+    clamped to max_blocks * 16, negative ones to 0: compared with the oracle
+    on the clamped lengths."""
+    q, kc, vc, table, _ = si.make_prefill_inputs(3, 4, 2, 40, [100, 60, 90], 64, "bf16", seed=6101, extra_blocks=2)
+    max_blocks = table.shape[1]
+    for lens in ([100, -3, 2 ** 31 - 1], [5000, 60, 0]):
+        given = torch.tensor(lens, dtype=torch.int32)
+        clamped = given.clamp(0, max_blocks * 16)
+        for causal in (True, False):
+            o, lse = run_prefill(q, kc, vc, table, given, causal)
+            ro, rl = orc.prefill_paged(f64(q), f64(kc), f64(vc), table.numpy(), clamped.numpy(), scale_for(64), causal)
+            assert_close("O", f64(o), ro, "bf16", "o")
+            assert_close("LSE", f64(lse), rl, "bf16", "lse")
 
 
 def test_prefill_equals_dense_forward_bitwise():

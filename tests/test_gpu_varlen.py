@@ -66,6 +66,8 @@ CASES = [
     ([129, 64, 17], [129, 64, 17], 2, 2, 128, "f32", True),
     ([700, 17, 1000], [700, 17, 1000], 8, 2, 128, "bf16", True),
     ([255, 256, 257, 1], [255, 256, 257, 1], 3, 3, 64, "bf16", False),
+    # 8-wave forward work-groups (B * Hq * 2 tiles of the longest >= 512)
+    ([300, 257, 100], [300, 257, 100], 128, 64, 128, "bf16", True),
 ]
 
 
