@@ -11,6 +11,18 @@ Tolerances (written once, here):
 * float16 / bfloat16 with large logits (Q, K scaled up): gradients can reach
   tens, where the storage rounding of a 16-bit output alone exceeds 5e-2, so
   they are held to max|x - ref| / max(1, max|ref|) <= 5e-2.
+* O of the large-logit workload (Q, K scaled by 8): its rows are nearly
+  one-hot, so O is close to single rows of V and the two bfloat16 roundings
+  the method makes (P before the second product, O at the end, each at most
+  2^-8 relative) reach 2 * 2^-8 * max|V|, about 0.04, beyond the N(0,1)
+  clause's 2e-2.  It is held instead to a bound derived per element from the
+  oracle's own P (``assert_o_within_rounding``): the worst case
+      |dO_ic| <= (1 + 2^-8) sum_j (2^-8 + 2 eps_i + g) P_ij |V_jc| + 2^-8 |O_ic|
+  with eps_i the float32 error bound of row i's scores (natural-log units,
+  d * 2^-24 * c * sum_d |q_id k_jd|, times 2 for the normalisation) and
+  g = Nk * 2^-24 for the float32 sums over keys; and, since each rounding is
+  uniform over half a spacing, rms(dO / sigma) <= 1 with
+  sigma_ic^2 = (2^-8)^2 (sum_j P_ij^2 V_jc^2 + O_ic^2) / 3.
 Rows that see no key must give LSE = -inf on both sides (and O = 0).
 """
 
@@ -89,3 +101,39 @@ def dtype_name(t: torch.Tensor) -> str:
 
 def scale_for(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+BF16_U = 2.0 ** -8   # unit roundoff of a 16-bit float with an 8-bit significand (bfloat16)
+F32_U = 2.0 ** -24
+
+
+def assert_o_within_rounding(what: str, got, q, k, v, scale: float, causal: bool, row_ids=None, nq_total=None):
+    """O of one (batch, head) within the per-element rounding bound described
+    in the module docstring.  q [nq, d] (the selected rows), k, v [nk, d], all
+    float64 holding the exact 16-bit inputs; got [nq, d].  Returns
+    (max abs error, rms of dO / sigma, max of dO / worst-case bound)."""
+    from oracle import attention_f64 as orc
+    got = np.asarray(got, dtype=np.float64)
+    p, lse = orc.attention_probs(q, k, scale, causal, row_ids, nq_total)
+    ref = p @ v
+    nk, d = k.shape
+    vis = orc.visible_mask(q.shape[0], nk, causal, row_ids, nq_total)
+    # Float32 score error of each row in natural-log units (worst case over its keys).
+    s_abs = abs(scale) * (np.abs(q) @ np.abs(k).T)
+    gamma_d = d * F32_U / (1 - d * F32_U)
+    eps = gamma_d * np.where(vis, s_abs, 0.0).max(axis=1) + 4 * F32_U
+    rel = BF16_U + 2 * eps[:, None] + nk * F32_U
+    worst = (1 + BF16_U) * ((rel * p) @ np.abs(v)) + BF16_U * np.abs(ref)
+    sigma = BF16_U * np.sqrt(((p * p) @ (v * v) + ref * ref) / 3.0)
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    empty = np.isneginf(lse)
+    assert (got[empty] == 0).all(), f"{what}: rows without keys must be 0"
+    err = np.abs(got - ref)
+    ratio = err / np.maximum(worst, 1e-300)
+    i, c = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio[i, c] <= 1.0, f"{what}: row {i} col {c} |dO| {err[i, c]:.4e} above its bound {worst[i, c]:.4e}"
+    live = sigma > 0
+    assert (err[~live] == 0).all(), f"{what}: error where no rounding can reach"
+    rms = float(np.sqrt(np.mean((err[live] / sigma[live]) ** 2))) if live.any() else 0.0
+    assert rms <= 1.0, f"{what}: rms(dO / sigma) = {rms:.3f} above 1"
+    return float(err.max()), rms, float(ratio[i, c])

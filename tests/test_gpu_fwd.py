@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import assert_close, dev, f64, scale_for
+from parity import assert_close, assert_o_within_rounding, dev, f64, scale_for
 from oracle import attention_f64 as orc
 import synth_inputs as si
 
@@ -132,20 +132,28 @@ def test_fwd_workload_gqa_bf16_4k():
 
 def test_fwd_workload_mha_bf16_16k():
     """Every row of four heads, the last included; the oracle takes the rows
-    in chunks of 2048 to bound host memory."""
+    in chunks of 2048 to bound host memory.  Large logits (Q, K x 8): O is
+    held to the per-element rounding bound of ``assert_o_within_rounding``,
+    LSE to 1e-3."""
     w = si.WORKLOADS["mha_bf16_16k"]
     q, k, v, _ = si.workload_attention_inputs(w)
     o, lse = run_fwd(q, k, v, True)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     g = w.Hq // w.Hkv
+    worst = 0.0
     for b, h in ((0, 0), (0, 5), (0, 11), (0, 15)):
-        kh, vh = f64(k[b:b + 1, h // g:h // g + 1]), f64(v[b:b + 1, h // g:h // g + 1])
+        kh, vh = f64(k[b, h // g]), f64(v[b, h // g])
         for r0 in range(0, w.Nq, 2048):
             rows = np.arange(r0, min(r0 + 2048, w.Nq))
-            o_ref, lse_ref = orc.attention_fwd(f64(q[b:b + 1, h:h + 1, rows]), kh, vh, w.scale, True,
-                                               row_ids=rows, nq_total=w.Nq)
-            assert_close(f"O[{b},{h}] rows {r0}..", f64(o[b:b + 1, h:h + 1, rows]), o_ref, w.dtype, "o")
-            assert_close(f"LSE[{b},{h}] rows {r0}..", f64(lse[b:b + 1, h:h + 1, rows]), lse_ref, w.dtype, "lse")
+            err, rms, ratio = assert_o_within_rounding(f"O[{b},{h}] rows {r0}..", f64(o[b, h, rows]),
+                                                       f64(q[b, h, rows]), kh, vh, w.scale, True,
+                                                       row_ids=rows, nq_total=w.Nq)
+            worst = max(worst, err)
+            _, lse_ref = orc.attention_probs(f64(q[b, h, rows]), kh, w.scale, True, row_ids=rows, nq_total=w.Nq)
+            assert_close(f"LSE[{b},{h}] rows {r0}..", f64(lse[b, h, rows]), lse_ref, w.dtype, "lse")
+            print(f"16k O[{b},{h}] rows {r0}..: max abs {err:.3e}, rms/sigma {rms:.3f}, max/bound {ratio:.3f}",
+                  flush=True)
+    print(f"16k forward: largest O abs error {worst:.4e}", flush=True)
 
 
 # Many heads of short sequences: B * Hq * ceil(Nq / 256) >= 2 * 256, so these
