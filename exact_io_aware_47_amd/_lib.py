@@ -25,6 +25,7 @@ _DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_GQA", 6: "FA_ERR_BLOCKSIZE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_SCALE", 10: "FA_ERR_ALIGN",
+    11: "FA_ERR_SCRATCH",
 }
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -50,6 +51,8 @@ SIGNATURES = {
     "flash_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
 }
 
 _lib = None
@@ -374,4 +377,37 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_spl
                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream(q.device))
     _check(code, "flash_attn_decode_paged")
+    return out, lse
+
+
+DECODE_SCRATCH_BYTES = 8 << 20  # FLASH_ATTN_DECODE_SCRATCH_BYTES
+
+
+def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_splits: int = 0, out=None,
+                         lse=None, want_lse: bool = True):
+    """decode_paged without a workspace: the library's fixed per-GPU scratch
+    area holds the split records (flash_attn_decode_paged_noalloc).  Pass
+    ``out`` (and ``lse``) to allocate nothing at all; calls that overlap on
+    one GPU race."""
+    _dense("q", q, ndim=3)
+    _dense("k_cache", k_cache, q.dtype, 4)
+    _dense("v_cache", v_cache, q.dtype, 4)
+    _dense("block_table", block_table, torch.int32, 2)
+    _dense("seq_lens", seq_lens, torch.int32, 1)
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    if v_cache.shape != k_cache.shape or k_cache.shape[3] != d or block_table.shape[0] != B or \
+            seq_lens.shape[0] != B:
+        raise ValueError("cache, table or lengths do not match q")
+    dev = _one_device(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, out=out,
+                      lse=lse)
+    out = _out("out", out, q.shape, q.dtype, dev)
+    if lse is not None or want_lse:
+        lse = _out("lse", lse, (B, Hq), torch.float32, dev)
+    code = lib().flash_attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                                 _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, d, bs, max_blocks,
+                                                 num_blocks, _default_scale(d, scale), int(num_splits),
+                                                 _dtype_code(q), _stream(q.device))
+    _check(code, "flash_attn_decode_paged_noalloc")
     return out, lse

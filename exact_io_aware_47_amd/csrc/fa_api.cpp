@@ -7,6 +7,8 @@
 
 #include "fa_kernels.h"
 
+static_assert(fa::kDecodeScratchBytes == FLASH_ATTN_DECODE_SCRATCH_BYTES, "scratch size out of sync with the header");
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // per tensor, keeps 32-bit element offsets valid
@@ -72,6 +74,7 @@ const char* flash_attn_strerror(int code) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes; LSE and int32 arrays 4 bytes)";
+    case FA_ERR_SCRATCH: return "the call needs more than the fixed scratch area of the allocation-free decode";
   }
   return "unknown error code";
 }
@@ -290,10 +293,15 @@ size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_
   return (size_t)B * Hq * splits * (d + 4) * sizeof(float);  // [O (d), m, l, 2 pad] per split
 }
 
-int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
-                            const int* seq_lens, void* O, float* LSE, int B, int Hq, int Hkv, int d, int block_size,
-                            int max_blocks_per_seq, int num_blocks, float scale, int num_splits, int dtype,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points, in the documented order up to
+// (not including) the workspace; on success *splits is the split count.
+int check_decode(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                 const int* seq_lens, const void* O, int B, int Hq, int Hkv, int d, int block_size,
+                 int max_blocks_per_seq, int num_blocks, float scale, int num_splits, int dtype, int* splits) {
   if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !O) return FA_ERR_NULL;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_splits < 0)
@@ -308,19 +316,64 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
       (int64_t)B * Hq * d >= kMaxElems || (int64_t)B * Hkv > 65535 || num_splits > kMaxDecodeSplits)
     return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  const int splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
-  if (!workspace ||
-      workspace_bytes < flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, splits))
-    return FA_ERR_WORKSPACE;
-  if (!aligned(Q, 16) || !aligned(K_cache, 16) || !aligned(V_cache, 16) || !aligned(O, 16) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(LSE, 4) || !aligned(workspace, 16))
-    return FA_ERR_ALIGN;
+  *splits = num_splits > 0 ? num_splits : flash_attn_decode_num_splits(B, Hkv, max_blocks_per_seq, block_size);
+  return FA_OK;
+}
+
+bool decode_ptrs_aligned(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                         const int* seq_lens, const void* O, const float* LSE) {
+  return aligned(Q, 16) && aligned(K_cache, 16) && aligned(V_cache, 16) && aligned(O, 16) &&
+         aligned(block_table, 4) && aligned(seq_lens, 4) && aligned(LSE, 4);
+}
+
+int run_decode(const void* Q, const void* K_cache, const void* V_cache, const int* block_table, const int* seq_lens,
+               void* O, float* LSE, int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+               int num_blocks, float scale, int splits, int dtype, void* part, void* stream) {
   fa::DecodeArgs a;
   a.q = Q; a.k_cache = K_cache; a.v_cache = V_cache; a.block_table = block_table; a.seq_lens = seq_lens;
-  a.o = O; a.lse = LSE; a.part = (float*)workspace;
+  a.o = O; a.lse = LSE; a.part = (float*)part;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.block_size = block_size; a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks; a.splits = splits; a.scale = scale; a.dtype = dtype;
   return launch_status(fa::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                            const int* seq_lens, void* O, float* LSE, int B, int Hq, int Hkv, int d, int block_size,
+                            int max_blocks_per_seq, int num_blocks, float scale, int num_splits, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int splits = 0;
+  const int st = check_decode(Q, K_cache, V_cache, block_table, seq_lens, O, B, Hq, Hkv, d, block_size,
+                              max_blocks_per_seq, num_blocks, scale, num_splits, dtype, &splits);
+  if (st != FA_OK) return st;
+  if (!workspace ||
+      workspace_bytes < flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, splits))
+    return FA_ERR_WORKSPACE;
+  if (!decode_ptrs_aligned(Q, K_cache, V_cache, block_table, seq_lens, O, LSE) || !aligned(workspace, 16))
+    return FA_ERR_ALIGN;
+  return run_decode(Q, K_cache, V_cache, block_table, seq_lens, O, LSE, B, Hq, Hkv, d, block_size,
+                    max_blocks_per_seq, num_blocks, scale, splits, dtype, workspace, stream);
+}
+
+int flash_attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,
+                                    const int* seq_lens, void* O, float* LSE, int B, int Hq, int Hkv, int d,
+                                    int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                                    int num_splits, int dtype, void* stream) {
+  int splits = 0;
+  const int st = check_decode(Q, K_cache, V_cache, block_table, seq_lens, O, B, Hq, Hkv, d, block_size,
+                              max_blocks_per_seq, num_blocks, scale, num_splits, dtype, &splits);
+  if (st != FA_OK) return st;
+  if (flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq, block_size, splits) >
+      FLASH_ATTN_DECODE_SCRATCH_BYTES)
+    return FA_ERR_SCRATCH;
+  if (!decode_ptrs_aligned(Q, K_cache, V_cache, block_table, seq_lens, O, LSE)) return FA_ERR_ALIGN;
+  void* part = nullptr;
+  if (fa::decode_scratch_area(&part) != hipSuccess) return FA_ERR_LAUNCH;
+  return run_decode(Q, K_cache, V_cache, block_table, seq_lens, O, LSE, B, Hq, Hkv, d, block_size,
+                    max_blocks_per_seq, num_blocks, scale, splits, dtype, part, stream);
 }
 
 }  // extern "C"

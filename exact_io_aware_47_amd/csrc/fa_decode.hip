@@ -25,6 +25,8 @@
 //   correction formula applied to every split against the common max):
 //     M = max m_s,  L = Σ l_s 2^(m_s - M),  O = Σ O_s 2^(m_s - M) / L,
 //     LSE = (M + log2 L) ln 2.
+#include <atomic>
+
 #include "fa_device.hpp"
 #include "fa_kernels.h"
 
@@ -350,7 +352,35 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Scratch area of the allocation-free decode entry point: the split records
+// ([B, Hq, splits, d + 4] float32) of one call.  Every GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses the
+// array's name as an address: decode_scratch_area() resolves the device copy
+// with hipGetSymbolAddress once per device and passes that pointer on.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+
 }  // namespace
+
+hipError_t decode_scratch_area(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    // With this device current: the address of this device's copy.  Racing
+    // first calls store the same value.
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dtype) {

@@ -95,4 +95,11 @@ constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Size of the fixed scratch area of the allocation-free decode (one per GPU).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+// Device address of the current device's scratch area (resolved once per
+// device, then cached).  The only HIP calls are hipGetDevice and, on a
+// device's first use, hipGetSymbolAddress.
+hipError_t decode_scratch_area(void** out);
+
 }  // namespace fa

@@ -78,8 +78,9 @@ enum fa_status {
   FA_ERR_WORKSPACE = 7, /* workspace pointer NULL or smaller than the size query says   */
   FA_ERR_LAUNCH = 8,    /* a kernel launch failed (hipGetLastError after the launch)    */
   FA_ERR_SCALE = 9,     /* scale is not finite                                          */
-  FA_ERR_ALIGN = 10     /* a pointer is misaligned: dtype tensors and workspaces need   */
+  FA_ERR_ALIGN = 10,    /* a pointer is misaligned: dtype tensors and workspaces need   */
                         /* 16-byte alignment, LSE and int32 arrays 4-byte alignment     */
+  FA_ERR_SCRATCH = 11   /* the allocation-free decode needs more than its fixed scratch */
 };
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -245,6 +246,34 @@ int flash_attn_decode_paged(const void* Q, const void* K_cache, const void* V_ca
                             int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
                             int num_blocks, float scale, int num_splits, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same inputs, outputs, semantics and
+ * kernels as flash_attn_decode_paged, without the workspace arguments: the
+ * split records live in a fixed scratch area of FLASH_ATTN_DECODE_SCRATCH_BYTES
+ * bytes that the library holds on every GPU it runs on until the process
+ * ends.  Its device address is resolved once per device, on the first call
+ * with that device current; nothing is allocated or freed by any call.
+ * Limit: flash_attn_decode_workspace_bytes(B, Hq, Hkv, d, max_blocks_per_seq,
+ * block_size, num_splits) must not exceed FLASH_ATTN_DECODE_SCRATCH_BYTES,
+ * else FA_ERR_SCRATCH (8 MiB holds, e.g., B = 8, Hq = 32, d = 128 with up to
+ * 62 splits).  Every call on a GPU shares that GPU's scratch area: calls that
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.  The scratch holds no state between calls (every record is rewritten
+ * before it is read).
+ * Errors (in this order): FA_ERR_NULL, FA_ERR_DTYPE, FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM, FA_ERR_GQA, FA_ERR_BLOCKSIZE, FA_ERR_SHAPE (too large),
+ * FA_ERR_SCALE, FA_ERR_SCRATCH, FA_ERR_ALIGN, FA_ERR_LAUNCH (also when the
+ * scratch address cannot be resolved).
+ */
+#define FLASH_ATTN_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+int flash_attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                                    const int* block_table, const int* seq_lens, void* O, float* LSE,
+                                    int B, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                                    int num_blocks, float scale, int num_splits, int dtype, void* stream);
 
 /*
  * Paged prefill: a chunk of Nq new queries per sequence attends to the

@@ -24,7 +24,7 @@ import torch
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-OK, NULL, SHAPE, HEADDIM, DTYPE, GQA, BLOCKSIZE, WORKSPACE, LAUNCH, SCALE, ALIGN = range(11)
+OK, NULL, SHAPE, HEADDIM, DTYPE, GQA, BLOCKSIZE, WORKSPACE, LAUNCH, SCALE, ALIGN, SCRATCH = range(12)
 F32, F16, BF16 = 0, 1, 2
 P = 0x10008  # fake, misaligned device pointer
 NAN, INF = float("nan"), float("inf")
@@ -69,7 +69,8 @@ def test_header_declares_the_entry_points():
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_decode_paged", "flash_attn_strerror",
               "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits",
               "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes",
-              "flash_attn_prefill_paged", "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_workspace_bytes"):
+              "flash_attn_prefill_paged", "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_workspace_bytes",
+              "flash_attn_decode_paged_noalloc"):
         assert n in names
 
 
@@ -83,7 +84,7 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_strerror(L):
-    for code in range(11):
+    for code in range(12):
         s = L.flash_attn_strerror(code)
         assert s and s != b"unknown error code"
     assert L.flash_attn_strerror(123) == b"unknown error code"
@@ -190,6 +191,27 @@ def test_decode_validation(L, kw, code):
     assert dec(L, **kw) == code
 
 
+def dec_na(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, bs=16, max_blocks=4,
+           nblocks=8, scale=0.1, splits=0, dtype=BF16):
+    return L.flash_attn_decode_paged_noalloc(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, d, bs, max_blocks, nblocks,
+                                             scale, splits, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(table=None), NULL), (dict(o=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(B=0), SHAPE), (dict(splits=-1), SHAPE), (dict(d=80), HEADDIM),
+    (dict(Hq=8, Hkv=3), GQA), (dict(bs=8), BLOCKSIZE), (dict(B=65536, Hkv=1, Hq=1), SHAPE),
+    (dict(B=1, max_blocks=1 << 27), SHAPE), (dict(scale=NAN), SCALE),
+    # the split records must fit the fixed 8 MiB scratch area
+    (dict(B=8, Hq=32, Hkv=8, splits=63, max_blocks=2048, nblocks=16384), SCRATCH),
+    (dict(B=8, Hq=32, Hkv=8, splits=1 << 16), SCRATCH),
+    (dict(B=8, Hq=32, Hkv=8, splits=62, max_blocks=2048, nblocks=16384), ALIGN),
+    (dict(), ALIGN), (dict(lse=None), ALIGN),
+])
+def test_decode_noalloc_validation(L, kw, code):
+    assert dec_na(L, **kw) == code
+
+
 def pre(L, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=64, d=128, bs=16, max_blocks=8,
         nblocks=20, scale=0.1, causal=1, dtype=BF16):
     return L.flash_attn_prefill_paged(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, Nq, d, bs, max_blocks, nblocks, scale,
@@ -284,6 +306,9 @@ def test_valid_calls_reach_the_launchers(L):
         lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=big),
         lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=None, ws=A, ws_bytes=big, splits=1 << 16),
         lambda: dec(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A, ws=A, ws_bytes=big, B=65535, Hq=1, Hkv=1),
+        lambda: dec_na(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=A),
+        lambda: dec_na(L, q=A, kc=A, vc=A, table=A, lens=A, o=A, lse=None, B=8, Hq=32, Hkv=8, splits=62,
+                       max_blocks=2048, nblocks=16384),
     ]
     for i, call in enumerate(calls):
         before = L.fa_stub_launch_count()
