@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libflash_attn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fa_api.cpp", "fa_device_query.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_device_query.cpp", "fa_fwd.hip", "fa_fwd_keysplit.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

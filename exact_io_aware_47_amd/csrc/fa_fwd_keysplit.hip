@@ -1,0 +1,379 @@
+// fa_fwd_keysplit.hip -- exact attention forward for gfx950, with the key
+// range of a query tile split between the two wave groups of a work-group.
+//
+// Same method as fa_fwd.hip (tutorial "FlashAttention and efficient
+// attention kernels": "Online softmax", "Correction formula", "Forward";
+// concept page "Flash-Attention", "Core idea"), combined with the split of
+// the key sequence that the tutorial's "Variant family" section describes for
+// FlashDecoding: partial softmax results over disjoint key ranges, merged
+// with the correction formula.
+//
+// Work decomposition.  A work-group of 8 waves owns kBR = 4 * RW query rows
+// of one (batch, query head).  Waves w and w + 4 (the same SIMD) own the same
+// RW rows: wave group 0 (waves 0-3) takes the key tiles 0, 2, 4, ... and
+// group 1 (waves 4-7) the tiles 1, 3, 5, ..., each with its own running
+// (max, sum, output).  At the end group 1 hands its partial results to
+// group 0 through LDS, which merges them (M = max(m0, m1),
+// l = l0 2^(m0-M) + l1 2^(m1-M), O likewise) and writes O and LSE.
+//
+// Time is cut into slots with one work-group barrier each.  In slot t the
+// group whose tiles have t's parity runs its matrix phase (Oᵀ += Vᵀ Pᵀ of its
+// previous tile t - 2, then Sᵀ = K Qᵀ of tile t) while the other group runs
+// the softmax of the tile it multiplied in slot t - 1, so each SIMD holds one
+// MFMA-phase and one VALU-phase wave ("ping-pong").  Slot t reads K(t) and
+// V(t - 2) and loads K(t + 1) and V(t - 1) into the other buffers.
+//
+// Each wave owns 32 rows and each tile 64 keys, as in the 8-wave kernel of
+// fa_fwd.hip; the difference is that a work-group covers 128 rows and takes
+// one tile per slot instead of one per two slots.  For grids with fewer than
+// two 256-row work-groups per compute unit this halves the serial chain of
+// tiles of a work-group while keeping the ping-pong (the 4-wave instance of
+// the 8-wave kernel has no partner wave on a SIMD).
+//
+// Layouts and the softmax follow fa_fwd.hip: queries on lanes (column of the
+// 32x32x16 product), the sigma row order that puts Pᵀ straight into the
+// B-operand layout, exp2 with scale*log2(e) folded into one FMA, and a
+// running max that moves only when it grows by more than 2^8.
+#include "fa_device.hpp"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+template <typename T, int D>
+struct KsCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kBR = 128;                          // query rows per work-group (32 per wave)
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBC = 64;                           // keys per tile
+  static constexpr int kKS = D / 16;                       // 16-wide k blocks along d
+  static constexpr int kMT = kBC / 32;                     // 32-key M tiles of Sᵀ
+  static constexpr int kPS = kBC / 16;                     // 16-key k blocks of Vᵀ Pᵀ
+  static constexpr int kDT = D / 32;                       // 32-row M tiles of Oᵀ
+  static constexpr int kTileBytes = kBC * kRowBytes;
+  static constexpr int kOFloats = kDT * 16;                // O accumulator floats per lane
+};
+
+struct KsParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* cu_q;  // packed batch: cumulative query / key counts [B + 1], else null
+  const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk;
+  int tot_q, tot_k;
+  float c;  // scale * log2(e)
+};
+
+constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
+
+// Schedule of NU fragment reads of RPU LDS instructions each, every fragment
+// feeding MPU MFMAs: the first PD fragments are read up front, then every
+// fragment's products are followed by the reads of the fragment PD places
+// later.
+template <int NU, int RPU, int MPU, int PD>
+__device__ __forceinline__ void sched_units() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  constexpr int pd = PD < NU ? PD : NU;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, RPU * pd, 0);
+#pragma unroll
+  for (int i = 0; i < NU - pd; i++) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, MPU, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, RPU, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, MPU * pd, 0);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_keysplit_kernel(KsParams p) {
+  using C = KsCfg<T, D>;
+  using E = Elem<T>;
+  using F = Frags<T>;
+  using TT = Tile<C::kRowBytes>;
+  typedef typename E::Frag Frag;
+  constexpr int KS = C::kKS, MT = C::kMT, PS = C::kPS, DT = C::kDT;
+
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes], k_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes], v_lds1[C::kTileBytes];
+  // Merge area: per group-0 wave, its partner's O floats (16-byte groups,
+  // lane-major) and its running max and sum.
+  __shared__ __attribute__((aligned(1024))) char mg_lds[4 * C::kOFloats * 64 * 4];
+  __shared__ __attribute__((aligned(1024))) char st_lds[4 * 2 * 64 * 4];
+  auto kbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? k_lds1 : k_lds0); };
+  auto vbuf = [&](int par) __attribute__((always_inline)) { return (lds_char*)(par ? v_lds1 : v_lds0); };
+
+  // Block -> (query tile, batch, head); causal: the heaviest tiles first.
+  const int bh_count = p.B * p.Hq;
+  const int id = blockIdx.x;
+  const int bh = id % bh_count;
+  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  const int Nq = sr.nq, Nk = sr.nk;
+  const int n_qt = (Nq + C::kBR - 1) / C::kBR;
+  if (id / bh_count >= n_qt) return;
+  const int qt = CAUSAL ? (n_qt - 1 - id / bh_count) : id / bh_count;
+
+  const int lane = lane_id(), w = wave_id();
+  const int G = w >> 2, wl = w & 3;  // wave group, wave within the group
+  const int h = lane >> 5, col = lane & 31;
+  const int q0 = qt * C::kBR;
+  const int qw = q0 + 32 * wl;       // first query row of this wave
+  const int qrow = qw + col;         // this lane's query row
+  const int diag = Nk - Nq;          // key j is visible to row i iff j <= i + diag (causal)
+
+  const size_t q_row0 = (size_t)p.Hq * sr.tq + (size_t)hq * Nq;
+  const size_t kv_row0 = (size_t)p.Hkv * sr.tk + (size_t)hkv * Nk;
+  const size_t q_slab = q_row0 * D;
+  const size_t kv_slab = kv_row0 * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + q_slab * 2, (uint32_t)Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
+
+  int n_tiles = (Nk + C::kBC - 1) / C::kBC;
+  if (CAUSAL) {
+    const int last_key = min(q0 + C::kBR, Nq) - 1 + diag;
+    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
+  }
+  auto dma_k = [&](int j, lds_char* dst) __attribute__((always_inline)) {
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  auto dma_v = [&](int j, lds_char* dst) __attribute__((always_inline)) {
+    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  if (n_tiles > 0) dma_k(0, kbuf(0));
+
+  // Qᵀ as the B operand of Sᵀ = K Qᵀ: lane holds row qrow, d = 16ks + 8h + 0..7.
+  Frag qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
+    if (p.c < 0.f) qf[ks] = E::negate(qf[ks]);
+  }
+
+  // Per-lane LDS offsets of the K row fragments (A rows are sigma-permuted
+  // keys) and of the Vᵀ column fragments.  The tile swizzle XORs a row's
+  // 16-byte chunk index with a per-row key, and row offsets are multiples of
+  // the row size (a power of two above every chunk offset used), so fragment
+  // ks of K lies at kbase ^ 32 ks and column tile dt of Vᵀ at
+  // vbase[u] ^ 64 dt: three registers and one XOR per read instead of one
+  // register per fragment.
+  uint32_t kbase = F::template row_off<TT>(sigma(col), 0, h);
+  uint32_t vbase[2] = {F::template col_off<TT>(0, 0, lane), F::template col_off<TT>(0, 1, lane)};
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++) o[dt] = f32x16{};
+  f32x16 s[MT];   // scores of this group's current tile
+  Frag pf[PS];    // its probabilities, consumed by the next matrix phase
+  float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
+  float l = 0.f;        // this lane's share of the running sum
+  const float c = p.c < 0.f ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+
+  // Does this wave see any key of tile j?
+  auto active = [&](int j) __attribute__((always_inline)) {
+    return j >= 0 && j < n_tiles && (!CAUSAL || j * C::kBC <= qw + 31 + diag);
+  };
+
+  auto gemm_pv = [&](const lds_char* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ps = 0; ps < PS; ps++)
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        const Frag a = F::lds_col_at(vb + 16 * ps * C::kRowBytes, vbase[0] ^ (uint32_t)(64 * dt),
+                                     vbase[1] ^ (uint32_t)(64 * dt));
+        o[dt] = E::mma(a, pf[ps], o[dt]);
+      }
+    sched_units<PS * DT, 2, 1, 2>();
+  };
+  auto gemm_s = [&](const lds_char* kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) s[mt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const Frag a = F::lds_row_at(kb + 32 * mt * C::kRowBytes, kbase ^ (uint32_t)(32 * ks));
+        s[mt] = E::mma(a, qf[ks], s[mt]);
+      }
+    sched_units<KS * MT, 1, 1, 2>();
+  };
+  // Register r of M tile mt holds key k0 + 32*mt + 16*(r/8) + 8h + (r%8).
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * C::kBC;
+    if ((k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > qw + diag)) {
+      const int horizon = CAUSAL ? min(qrow + diag, Nk - 1) : Nk - 1;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int key = k0 + 32 * mt + 16 * (r >> 3) + 8 * h + (r & 7);
+          if (key > horizon) s[mt][r] = -INFINITY;
+        }
+    }
+    // Four independent three-input max chains; c > 0, so max(c s) = c max(s).
+    float x[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
+    const float mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * c;
+    // Move the running max only if it grows by more than kTau.
+    const bool grow = mx > m + kTau;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m - mx) : 1.f;
+      m = grow ? mx : m;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;  // rows that have seen no key yet
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        s[mt][r] = fast_exp2(fmaf(s[mt][r], c, -m_use));
+        rs[r & 3] += s[mt][r];
+      }
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    // Pᵀ k block ps = registers 8*(ps%2).. of M tile ps/2.
+#pragma unroll
+    for (int ps = 0; ps < PS; ps++) {
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 8; t++) pv[t] = s[ps >> 1][8 * (ps & 1) + t];
+      pf[ps] = E::pack(pv);
+    }
+  };
+
+  // ---- slot schedule (one barrier per slot).  Slot t: loads of K(t + 1)
+  // and V(t - 1); the group of parity t runs its matrix phase (PV of tile
+  // t - 2, S of tile t), the other group the softmax of tile t - 1.  Slots are
+  // unrolled by two so that every buffer is a compile-time object, and each
+  // group runs its own copy of the loop, so every slot is straight-line code.
+  const int n_slots = n_tiles + 2;
+  auto slot = [&](auto gc, auto pc, int t) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value;    // this wave's group
+    constexpr int par = decltype(pc)::value;  // parity of t
+    // The lane offsets are re-hidden from the compiler at every slot, so
+    // that it adds them to the buffer bases inside the slot instead of
+    // keeping one hoisted address register per (buffer, fragment) pair.
+    asm volatile("" : "+v"(kbase), "+v"(vbase[0]), "+v"(vbase[1]));
+    if (t + 1 < n_tiles) dma_k(t + 1, kbuf(par ^ 1));
+    if (t >= 1 && t - 1 < n_tiles) dma_v(t - 1, vbuf(par ^ 1));
+    if constexpr (g == par) {
+      if (active(t - 2)) gemm_pv(vbuf(par));
+      if (active(t)) gemm_s(kbuf(par));
+    } else {
+      if (active(t - 1)) softmax(t - 1);
+    }
+    wait_vmem();
+    barrier_lds();
+  };
+  wait_vmem();
+  barrier_lds();
+  auto run = [&](auto gc) __attribute__((always_inline)) {
+    for (int t = 0; t < n_slots; t += 2) {
+      slot(gc, Int<0>{}, t);
+      slot(gc, Int<1>{}, t + 1);
+    }
+  };
+  if (G == 0) run(Int<0>{});
+  else run(Int<1>{});
+
+  // ---- merge: group 1 hands (O, m, l) to the group-0 wave with its rows;
+  // that wave rescales both parts to the common max and adds them.
+  lds_char* const mg = (lds_char*)mg_lds + wl * C::kOFloats * 64 * 4;
+  __attribute__((address_space(3))) float* const st =
+      (__attribute__((address_space(3))) float*)((lds_char*)st_lds + wl * 2 * 64 * 4);
+  if (G == 1) {
+    st[lane] = m;
+    st[64 + lane] = l;
+#pragma unroll
+    for (int f4 = 0; f4 < C::kOFloats / 4; f4++) {
+      const int dt = f4 / 4, r = 4 * (f4 % 4);
+      *(__attribute__((address_space(3))) f32x4*)(mg + (f4 * 64 + lane) * 16) =
+          f32x4{o[dt][r], o[dt][r + 1], o[dt][r + 2], o[dt][r + 3]};
+    }
+  }
+  barrier_lds();
+  if (G == 1) return;
+  {
+    const float m1 = st[lane], l1 = st[64 + lane];
+    const float M = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+    l = a0 * l + a1 * l1;
+    m = M;
+#pragma unroll
+    for (int f4 = 0; f4 < C::kOFloats / 4; f4++) {
+      const int dt = f4 / 4, r = 4 * (f4 % 4);
+      const f32x4 v4 = *(__attribute__((address_space(3))) f32x4*)(mg + (f4 * 64 + lane) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[dt][r + i] = fmaf(a1, v4[i], a0 * o[dt][r + i]);
+    }
+  }
+
+  // ---- epilogue (group 0): O = Oᵀ / l, LSE = m + log2(l) in natural log.
+  const float lt = sum_halves(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((char*)p.o + q_slab * 2, (uint32_t)Nq * C::kRowBytes);
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const int d0 = 32 * dt + 8 * a4 + 4 * h;
+      F::store4(ro, (uint32_t)qrow * C::kRowBytes + d0 * 2, o[dt][4 * a4] * inv, o[dt][4 * a4 + 1] * inv,
+                o[dt][4 * a4 + 2] * inv, o[dt][4 * a4 + 3] * inv);
+    }
+  if (h == 0) {
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + q_row0, (uint32_t)Nq * 4);
+    const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+    buf_store4(rl, (uint32_t)qrow * 4, __builtin_bit_cast(uint32_t, lse));
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
+  using C = KsCfg<T, D>;
+  KsParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
+  p.cu_q = a.cu_q; p.cu_k = a.cu_k;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.tot_q = a.tot_q; p.tot_k = a.tot_k;
+  p.c = a.scale * kLog2e;
+  const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_keysplit_kernel<T, D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 32: return a.causal ? launch_typed<T, 32, true>(a, s) : launch_typed<T, 32, false>(a, s);
+    case 64: return a.causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
+    case 128: return a.causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_keysplit(const FwdArgs& a, hipStream_t stream) {
+  if (a.block_table != nullptr) return hipErrorInvalidValue;  // dense and packed batches only
+  switch (a.dtype) {
+    case 1: return launch_d<_Float16>(a, stream);
+    case 2: return launch_d<__bf16>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -73,14 +73,9 @@ def test_prefill_clamps_out_of_range_lengths():
             assert_close("LSE", f64(lse), rl, "bf16", "lse")
 
 
-def test_prefill_equals_dense_forward_bitwise():
-    """Keys scattered into pages by host code: the paged call gives bitwise
-    the dense forward's O and LSE (same tiles, same arithmetic order)."""
-    fa = _fa()
-    B, Hq, Hkv, N, d = 2, 4, 2, 333, 128
-    q, k, v, _ = si.make_attention_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=93)
+def _scatter_into_pages(k, v, B, Hkv, N, d, seed):
     nb = -(-N // 16)
-    perm = torch.randperm(B * nb + 3, generator=torch.Generator().manual_seed(94))
+    perm = torch.randperm(B * nb + 3, generator=torch.Generator().manual_seed(seed))
     table = perm[: B * nb].view(B, nb).to(torch.int32)
     kc = torch.zeros(B * nb + 3, Hkv, 16, d, dtype=k.dtype)
     vc = torch.zeros_like(kc)
@@ -88,12 +83,43 @@ def test_prefill_equals_dense_forward_bitwise():
         for t in range(N):
             kc[table[b, t // 16], :, t % 16] = k[b, :, t]
             vc[table[b, t // 16], :, t % 16] = v[b, :, t]
+    return kc, vc, table
+
+
+def test_prefill_equals_dense_forward_bitwise():
+    """Keys scattered into pages by host code: on a grid that runs the 8-wave
+    kernel for both (B * Hq * ceil(N / 256) >= 512), the paged call gives
+    bitwise the dense forward's O and LSE (same tiles, same arithmetic
+    order)."""
+    fa = _fa()
+    B, Hq, Hkv, N, d = 2, 128, 64, 333, 128
+    assert B * Hq * -(-N // 256) >= 512
+    q, k, v, _ = si.make_attention_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=93)
+    kc, vc, table = _scatter_into_pages(k, v, B, Hkv, N, d, 94)
     lens = torch.full((B,), N, dtype=torch.int32)
     for causal in (True, False):
         o, lse = fa.fwd(dev(q), dev(k), dev(v), causal=causal)
         po, pl = fa.prefill_paged(dev(q), dev(kc), dev(vc), dev(table), dev(lens), causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(o, po) and torch.equal(lse, pl)
+
+
+def test_prefill_and_dense_forward_on_a_short_grid():
+    """A short grid: the dense call runs the key-split kernel, the paged call
+    the 4-wave kernel; both match the oracle."""
+    fa = _fa()
+    B, Hq, Hkv, N, d = 2, 4, 2, 333, 128
+    q, k, v, _ = si.make_attention_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=93)
+    kc, vc, table = _scatter_into_pages(k, v, B, Hkv, N, d, 94)
+    lens = torch.full((B,), N, dtype=torch.int32)
+    for causal in (True, False):
+        o, lse = fa.fwd(dev(q), dev(k), dev(v), causal=causal)
+        po, pl = fa.prefill_paged(dev(q), dev(kc), dev(vc), dev(table), dev(lens), causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = orc.attention_fwd(f64(q), f64(k), f64(v), scale_for(d), causal)
+        for name, got, ref, kind in (("O", o, ro, "o"), ("LSE", lse, rl, "lse"), ("paged O", po, ro, "o"),
+                                     ("paged LSE", pl, rl, "lse")):
+            assert_close(name, f64(got.cpu()), ref, "bf16", kind)
 
 
 def test_prefill_bad_table_entry_reads_zero_page():
