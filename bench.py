@@ -145,6 +145,17 @@ def measured_traffic(kernel: str):
 
 
 # ---------------------------------------------------------------------------
+def mfma_roof():
+    """Build bench_mfma_roof.hip for gfx950 into _build/ and run it (2048
+    work-groups of 8 waves, 4000 iterations per wave)."""
+    import subprocess
+    exe = os.path.join(ROOT, "_build", "bench_mfma_roof")
+    os.makedirs(os.path.dirname(exe), exist_ok=True)
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    os.path.join(ROOT, "bench_mfma_roof.hip"), "-o", exe], check=True)
+    return subprocess.run([exe, "2048", "4000"]).returncode
+
+
 def ensure_library():
     from exact_io_aware_47_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):
@@ -424,6 +435,65 @@ KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_ke
                ("fp8_vt_kernel", "fp8"), ("fwd_fp8_kernel", "fp8"))
 
 
+# The benchmark's legs in the order main() runs them, with the kernel
+# dispatches of one step of each (warm-up and timed steps alike).
+LEG_ORDER = (("mha_f32_small (non-causal)", 4), ("mha_f16 (causal)", 4), ("mha_f16 (non-causal)", 4),
+             ("mha_bf16_16k", 4), ("varlen_bf16", 4), ("prefill_paged_bf16", 1), ("mha_fp8_4k", 2),
+             ("decode_gqa_paged", 2), ("gqa_bf16_4k", 4), ("mha_bf16_4k", 4))
+ATTENTION_KERNEL = ("fwd_kernel", "fwd_keysplit_kernel", "fwd_fp8_kernel", "fp8_vt_kernel", "bwd_prep_kernel",
+                    "bwd_dkdv16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel",
+                    "decode_reduce_kernel")
+
+
+def _short_kernel_name(n):
+    """Kernel name with its template arguments, from a mangled or demangled name."""
+    import re
+    m = re.search(r"N_1\d+(\w+?_kernel)I(.*?)EEv", n)
+    if m:
+        args = []
+        for tok in re.findall(r"DF16b|DF16_|Lb[01]E|Li\d+E|^f|(?<=E)f", m.group(2)):
+            args.append({"DF16b": "bf16", "DF16_": "f16", "f": "float", "Lb1E": "1", "Lb0E": "0"}.get(
+                tok, tok[2:-1] if tok.startswith("Li") else tok))
+        return f"{m.group(1)}<{', '.join(args)}>"
+    m = re.search(r"::(\w+_kernel)<([^>]*)>", n)
+    return f"{m.group(1)}<{m.group(2).replace('true', '1').replace('false', '0')}>" if m else n[:60]
+
+
+def trace_summary(trace_csv, steps, warmup):
+    """Markdown table of a rocprofv3 kernel trace of one default benchmark
+    run: every attention dispatch labelled with its leg (legs run in
+    LEG_ORDER, each with warmup + steps steps), per (leg, kernel) the call
+    count, the average over all calls and over the timed (last `steps`)
+    calls, min, max and total."""
+    import collections
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    legs = [(n, k * (warmup + steps)) for n, k in LEG_ORDER]
+    leg_i, used = 0, 0
+    g = collections.defaultdict(list)
+    for r in rows:
+        n = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        if not any(k in n for k in ATTENTION_KERNEL):
+            g[("(torch / runtime)", _short_kernel_name(n))].append(dur)
+            continue
+        while leg_i < len(legs) and used >= legs[leg_i][1]:
+            leg_i, used = leg_i + 1, 0
+        leg = legs[leg_i][0] if leg_i < len(legs) else "?"
+        used += 1
+        g[(leg, _short_kernel_name(n))].append(dur)
+    tot = sum(sum(v) for v in g.values())
+    out = [f"| workload | kernel (template arguments) | calls | avg us | avg us, last {steps} (timed) calls | "
+           "min us | max us | total us | % |", "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (leg, k), v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        t = v[-steps:]
+        out.append(f"| {leg} | `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {sum(t) / len(t):.2f} | {min(v):.2f} | "
+                   f"{max(v):.2f} | {sum(v):.1f} | {100 * sum(v) / tot:.1f} |")
+    text = "\n".join(out)
+    print(text)
+    return text
+
+
 def _counter_sums(path, counter):
     """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 CSV."""
     import csv
@@ -483,6 +553,74 @@ def util_from(csv_path, out_dir=None):
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
     return rec
+
+
+# Labels of the counter tables, and the algorithmic flops each kernel's work
+# amounts to on its workload (mha_bf16_4k for the training kernels and the FP8
+# forward's shape; the decode is HBM-bound).
+COUNTER_ROWS = (("fwd", "fwd (`fwd_kernel<bf16,128,causal>`)", "1.375e11"), ("prep", "prep", "—"),
+                ("dkdv", "dkdv (`bwd_dkdv16_kernel`)", "2.750e11"),
+                ("dq", "dq (`bwd_dq_kernel`)", "0.687e11 (2d; S and dP recomputed)"),
+                ("decode", "decode (`decode_split_kernel`)", "— (HBM-bound)"),
+                ("fp8", "fp8 (`fwd_fp8_kernel`)", "1.375e11"))
+
+
+def _last_launch_counters(csv_path):
+    """{key: (counters, us)} of the last dispatch of each kernel key (decode:
+    its split kernel; FP8: its forward kernel, not the V staging)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {},
+                                                       "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    last = {}
+    for _, d in sorted(per.items()):
+        if "decode_reduce" in d["name"] or "fp8_vt" in d["name"]:
+            continue
+        key = next((k for pat, k in KERNEL_KEYS if pat in d["name"]), None)
+        if key is not None:
+            last[key] = (d["c"], d["us"])
+    return last
+
+
+def util_table(csv_path):
+    """Markdown rows of the MFMA-busy / clock / LDS counter table (last launch of each kernel)."""
+    last = _last_launch_counters(csv_path)
+    rows = ["| kernel | µs | MFMA busy | clock GHz | LDS bank conflicts / access | LDS wait / LDS active | "
+            "executed flops | algorithmic flops |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for key, label, alg in COUNTER_ROWS:
+        if key not in last:
+            continue
+        c, us = last[key]
+        grbm = c["GRBM_GUI_ACTIVE"] / XCDS
+        clock = grbm / (us * 1e3)
+        valid = clock <= MAX_SHADER_GHZ
+        busy = f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (grbm * SIMDS):.1f}%" if valid else "—"
+        bc = c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"])
+        wa = c["SQ_WAIT_INST_LDS"] / max(1.0, c["SQ_ACTIVE_INST_LDS"])
+        fl = c["SQ_INSTS_VALU_MFMA_MOPS_F8" if key == "fp8" else "SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        fls = (f"{fl:.3e}" + (" (F8)" if key == "fp8" else "")) if fl else "0"
+        rows.append(f"| {label} | {us:.1f} | {busy} | {f'{clock:.2f}' if valid else '—'} | {bc:.3f} | {wa:.2f} | "
+                    f"{fls} | {alg} |")
+    return "\n".join(rows)
+
+
+def issue_table(csv_path):
+    """Markdown rows of where the waves' time goes (SQ counters over SQ_WAVE_CYCLES, last launch)."""
+    last = _last_launch_counters(csv_path)
+    rows = ["| kernel | µs | issuing | waiting on a dependency | waiting for an issue slot | VALU | LDS | VMEM |",
+            "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for key, label, _ in COUNTER_ROWS:
+        if key not in last:
+            continue
+        c, us = last[key]
+        w = max(1.0, c["SQ_WAVE_CYCLES"])
+        f = lambda n: f"{100 * c[n] / w:.0f}%"
+        rows.append(f"| {label} | {us:.1f} | {f('SQ_ACTIVE_INST_ANY')} | {f('SQ_WAIT_ANY')} | {f('SQ_WAIT_INST_ANY')} | "
+                    f"{f('SQ_ACTIVE_INST_VALU')} | {f('SQ_ACTIVE_INST_LDS')} | {100 * c['SQ_ACTIVE_INST_VMEM'] / w:.1f}% |")
+    return "\n".join(rows)
 
 
 def traffic_from(fetch_csv, write_csv, out_dir=None):
@@ -558,13 +696,30 @@ def main(argv=None):
                     help="write profiles/mfma_util.json from a rocprofv3 counter CSV of --profile-once")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 counter CSVs")
+    ap.add_argument("--mfma-roof", action="store_true",
+                    help="build and run bench_mfma_roof.hip: the bf16 MFMA rate sustained with constant and random operands")
+    ap.add_argument("--util-table", metavar="COUNTER_CSV", help="print the MFMA-busy / LDS counter table")
+    ap.add_argument("--issue-table", metavar="COUNTER_CSV", help="print the issue-breakdown counter table")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-leg table of a rocprofv3 kernel trace of a run with these --steps/--warmup")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps, args.warmup)
+        return 0
+    if args.util_table:
+        print(util_table(args.util_table))
+        return 0
+    if args.issue_table:
+        print(issue_table(args.issue_table))
+        return 0
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return 0
     if args.util_from:
         util_from(args.util_from)
         return 0
+    if args.mfma_roof:
+        return mfma_roof()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention kernels here are "
               "built and timed on a single MI355X and no multi-GPU path exists.", file=sys.stderr)
@@ -582,16 +737,11 @@ def main(argv=None):
         profile_once(torch, fa, si, max(1, args.profile_repeats))
         return 0
 
-    # The other legs run first: the headline step is timed last, on a GPU whose
-    # clock has settled under the same kind of work (an idle MI355X runs these
+    # The legs run in LEG_ORDER: the headline step is timed last, right after
+    # the grouped-query step, which runs the same kernels, so that it meets a
+    # GPU whose clock has settled under this work (an idle MI355X runs these
     # kernels ~10% slower over its first tens of milliseconds of such a burst).
     extra = {}
-    # The grouped-query training shape (four query heads per K/V head), same step.
-    wg, ms_g, per_g, _ = bench_training(torch, fa, si, args.steps, args.warmup, "gqa_bf16_4k")
-    flg = attention_flops(wg.B, wg.Hq, wg.Nq, wg.Nk, wg.d, True)
-    extra["gqa"] = {"workload": "gqa_bf16_4k: causal forward + backward, B=2 Hq=32 Hkv=8 N=4096 d=128 bf16",
-                   "TFLOP/s": round((flg["fwd"] + flg["dkdv"] + flg["dq"]) / (ms_g * 1e-3) / 1e12, 2),
-                   "ms_per_step": round(ms_g, 4), "us": {n: round(v * 1e3, 2) for n, v in per_g.items()}}
     # The other attention configurations, same step, each against its dtype's matrix peak.
     extra["configs"] = {}
     for cname, causal in (("mha_f32_small", False), ("mha_f16", True), ("mha_f16", False), ("mha_bf16_16k", True)):
@@ -644,6 +794,12 @@ def main(argv=None):
                           "roofline": {"kernel": "decode (split + reduce)", "bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": PEAK_HBM, "unit": "GB/s", "frac": round(gbs / PEAK_HBM, 4),
                                        "traffic": measured_traffic("decode")}}
+    # The grouped-query training shape (four query heads per K/V head), same step.
+    wg, ms_g, per_g, _ = bench_training(torch, fa, si, args.steps, args.warmup, "gqa_bf16_4k")
+    flg = attention_flops(wg.B, wg.Hq, wg.Nq, wg.Nk, wg.d, True)
+    extra["gqa"] = {"workload": "gqa_bf16_4k: causal forward + backward, B=2 Hq=32 Hkv=8 N=4096 d=128 bf16",
+                   "TFLOP/s": round((flg["fwd"] + flg["dkdv"] + flg["dq"]) / (ms_g * 1e-3) / 1e12, 2),
+                   "ms_per_step": round(ms_g, 4), "us": {n: round(v * 1e3, 2) for n, v in per_g.items()}}
     w, ms_step, per, wall = bench_training(torch, fa, si, args.steps, args.warmup)
     fl = attention_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, True)
     step_flops = fl["fwd"] + fl["dkdv"] + fl["dq"]

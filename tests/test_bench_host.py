@@ -99,3 +99,25 @@ def test_traffic_from_scales_by_the_calibration_copy(tmp_path):
     assert rec["decode"]["fetch_bytes"] == (200 + 10) * 1024 * 2
     assert rec["decode"]["write_bytes"] == (4 + 1) * 1024
     assert os.path.exists(tmp_path / "traffic.json") and os.path.exists(tmp_path / "hbm_traffic_mha_bf16_4k_decode_fp8.md")
+
+
+def test_trace_summary_labels_dispatches_by_leg(tmp_path):
+    """Dispatches are assigned to legs in LEG_ORDER by their counts."""
+    import csv
+    steps, warmup = 2, 1
+    rows, t = [], 0
+    names = {"fwd": "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELb1ELb0ELi8EEEvNS0_9FwdParamsEPKiS4_",
+             "other": "at::native::elementwise_kernel"}
+    for leg, per_step in bench.LEG_ORDER:
+        for _ in range((steps + warmup) * per_step):
+            rows.append((names["fwd"], t, t + 1000 if leg != "mha_bf16_4k" else t + 3000))
+            t += 5000
+    rows.append((names["other"], t, t + 500))
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerows(rows)
+    text = bench.trace_summary(str(tmp_path / "trace.csv"), steps, warmup)
+    line = [l for l in text.splitlines() if l.startswith("| mha_bf16_4k |")][0]
+    assert "`fwd_kernel<bf16, 128, 1, 0, 8>`" in line and "| 12 | 3.00 | 3.00 |" in line
+    assert any(l.startswith("| (torch / runtime) |") for l in text.splitlines())
