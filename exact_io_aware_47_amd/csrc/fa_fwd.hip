@@ -478,16 +478,16 @@ hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
 }
 
 // 8-wave work-groups unless that grid gives fewer than two per compute unit
-// of the device.  Such short grids run, for 16-bit types over contiguous K/V,
-// the kernel whose two wave groups split each 128-row tile's keys (half the
-// serial chain of tiles per work-group, the ping-pong kept); otherwise the
-// 4-wave instance of this kernel.
+// of the device.  Such short grids run, for 16-bit types, the kernel whose
+// two wave groups split each 128-row tile's keys (half the serial chain of
+// tiles per work-group, the ping-pong kept); float32 runs the 4-wave
+// instance of this kernel.
 template <typename T, int D>
 hipError_t launch_waves(const FwdArgs& a, hipStream_t s) {
   const int64_t grid8 = (int64_t)((a.Nq + FwdCfg<T, D, 8>::kBR - 1) / FwdCfg<T, D, 8>::kBR) * a.B * a.Hq;
   if (grid8 >= 2 * (int64_t)a.cus) return launch_mask<T, D, 8>(a, s);
-  if (Elem<T>::kBytes == 2 && a.block_table == nullptr) return launch_fwd_keysplit(a, s);
-  return launch_mask<T, D, 4>(a, s);
+  if constexpr (Elem<T>::kBytes == 2) return launch_fwd_keysplit(a, s);
+  else return launch_mask<T, D, 4>(a, s);
 }
 
 template <typename T>

@@ -23,8 +23,10 @@
 // MFMA-phase and one VALU-phase wave ("ping-pong").  Slot t reads K(t) and
 // V(t - 2) and loads K(t + 1) and V(t - 1) into the other buffers.
 //
-// Each wave owns 32 rows and each tile 64 keys, as in the 8-wave kernel of
-// fa_fwd.hip; the difference is that a work-group covers 128 rows and takes
+// K and V come from contiguous tensors (dense or packed batches) or, with
+// PAGED, from 16-token pages through the block table, staged page by page
+// as in fa_fwd.hip.  Each wave owns 32 rows and each tile 64 keys, as in the
+// 8-wave kernel of fa_fwd.hip; the difference is that a work-group covers 128 rows and takes
 // one tile per slot instead of one per two slots.  For grids with fewer than
 // two 256-row work-groups per compute unit this halves the serial chain of
 // tiles of a work-group while keeping the ping-pong (the 4-wave instance of
@@ -64,6 +66,10 @@ struct KsParams {
   const int* cu_k;
   int B, Hq, Hkv, Nq, Nk;
   int tot_q, tot_k;
+  // Paged KV (k, v are the page caches [num_blocks, Hkv, 16, D]): the block
+  // table [B, max_blocks] and cached tokens per sequence are kernel arguments
+  // of their own (restrict-qualified, read through the scalar cache).
+  int max_blocks, num_blocks;
   float c;  // scale * log2(e)
 };
 
@@ -86,9 +92,11 @@ __device__ __forceinline__ void sched_units() {
   __builtin_amdgcn_sched_group_barrier(kMfma, MPU * pd, 0);
 }
 
-template <typename T, int D, bool CAUSAL>
+// PAGED: K and V are read from a paged cache through the block table; the
+// queries are the last Nq positions of each sequence (dense Q, O, LSE).
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_keysplit_kernel(KsParams p) {
+void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const int* __restrict__ seq_lens) {
   using C = KsCfg<T, D>;
   using E = Elem<T>;
   using F = Frags<T>;
@@ -111,7 +119,14 @@ void fwd_keysplit_kernel(KsParams p) {
   const int bh = id % bh_count;
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
-  const SeqRows sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  SeqRows sr;
+  if constexpr (PAGED) {
+    // Cached tokens of the sequence, clamped to what its table row can address.
+    const int n = min(max(seq_lens[b], 0), p.max_blocks * 16);
+    sr = SeqRows{p.Nq, n, b * p.Nq, 0};
+  } else {
+    sr = seq_rows(p.cu_q, p.cu_k, b, p.Nq, p.Nk, p.tot_q, p.tot_k);
+  }
   const int Nq = sr.nq, Nk = sr.nk;
   const int n_qt = (Nq + C::kBR - 1) / C::kBR;
   if (id / bh_count >= n_qt) return;
@@ -138,13 +153,46 @@ void fwd_keysplit_kernel(KsParams p) {
     const int last_key = min(q0 + C::kBR, Nq) - 1 + diag;
     n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::kBC + 1);
   }
-  auto dma_k = [&](int j, lds_char* dst) __attribute__((always_inline)) {
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  // Paged KV: the rows a wave moves of any tile lie in one 16-token page;
+  // PageRef is that page for one tile (byte offset of its (page, kv head)
+  // block in the cache and bytes of valid rows; 0 bytes reads zeros).
+  struct PageRef {
+    size_t off;
+    uint32_t bytes;
   };
-  auto dma_v = [&](int j, lds_char* dst) __attribute__((always_inline)) {
-    dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  const int wrow0 = dma_wave_row0<C::kRowBytes, C::kBC, C::kWaves>(w);
+  const int* trow = PAGED ? block_table + (size_t)b * p.max_blocks : nullptr;
+  auto page_of = [&](int jj) __attribute__((always_inline)) {
+    PageRef r{0, 0u};
+    if constexpr (PAGED) {
+      const int t0 = jj * C::kBC + wrow0;  // first token of this wave's rows
+      if (jj >= 0 && jj < n_tiles && t0 < Nk) {
+        const int pid = trow[t0 >> 4];
+        if (pid >= 0 && pid < p.num_blocks) {  // a bad table entry reads as a page of zeros
+          r.off = ((size_t)pid * p.Hkv + hkv) * (16 * C::kRowBytes);
+          r.bytes = (uint32_t)min(16, Nk - (t0 & ~15)) * C::kRowBytes;
+        }
+      }
+    }
+    return r;
   };
-  if (n_tiles > 0) dma_k(0, kbuf(0));
+  auto dma_k = [&](int j, lds_char* dst, const PageRef& pr) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves, true>(make_rsrc((const char*)p.k + pr.off, pr.bytes), 0u, dst, w,
+                                                      lane);
+    else
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rk, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  auto dma_v = [&](int j, lds_char* dst, const PageRef& pr) __attribute__((always_inline)) {
+    if constexpr (PAGED)
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves, true>(make_rsrc((const char*)p.v + pr.off, pr.bytes), 0u, dst, w,
+                                                      lane);
+    else
+      dma_tile<C::kRowBytes, C::kBC, C::kWaves>(rv, (uint32_t)j * C::kBC * C::kRowBytes, dst, w, lane);
+  };
+  // Pages of the tiles the next slot loads: K(t + 1) and V(t - 1) for slot t.
+  PageRef pg_k = page_of(1), pg_v = page_of(-1);
+  if (n_tiles > 0) dma_k(0, kbuf(0), page_of(0));
 
   // Qᵀ as the B operand of Sᵀ = K Qᵀ: lane holds row qrow, d = 16ks + 8h + 0..7.
   Frag qf[KS];
@@ -266,13 +314,21 @@ void fwd_keysplit_kernel(KsParams p) {
     // that it adds them to the buffer bases inside the slot instead of
     // keeping one hoisted address register per (buffer, fragment) pair.
     asm volatile("" : "+v"(kbase), "+v"(vbase[0]), "+v"(vbase[1]));
-    if (t + 1 < n_tiles) dma_k(t + 1, kbuf(par ^ 1));
-    if (t >= 1 && t - 1 < n_tiles) dma_v(t - 1, vbuf(par ^ 1));
+    if (t + 1 < n_tiles) dma_k(t + 1, kbuf(par ^ 1), pg_k);
+    if (t >= 1 && t - 1 < n_tiles) dma_v(t - 1, vbuf(par ^ 1), pg_v);
     if constexpr (g == par) {
       if (active(t - 2)) gemm_pv(vbuf(par));
       if (active(t)) gemm_s(kbuf(par));
     } else {
       if (active(t - 1)) softmax(t - 1);
+    }
+    if constexpr (PAGED) {
+      // Table entries of the next slot's tiles, read after this slot's LDS
+      // work (the empty asm keeps them there) so that their wait merges with
+      // the barrier's.
+      asm volatile("" ::: "memory");
+      pg_k = page_of(t + 2);
+      pg_v = page_of(t);
     }
     wait_vmem();
     barrier_lds();
@@ -340,7 +396,7 @@ void fwd_keysplit_kernel(KsParams p) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   using C = KsCfg<T, D>;
   KsParams p;
@@ -348,19 +404,28 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
+  p.max_blocks = a.max_blocks; p.num_blocks = a.num_blocks;
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_keysplit_kernel<T, D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);
+  hipLaunchKernelGGL((fwd_keysplit_kernel<T, D, CAUSAL, PAGED>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,
+                     a.block_table, a.seq_lens);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_mask(const FwdArgs& a, hipStream_t s) {
+  if (a.block_table)
+    return a.causal ? launch_typed<T, D, true, true>(a, s) : launch_typed<T, D, false, true>(a, s);
+  return a.causal ? launch_typed<T, D, true, false>(a, s) : launch_typed<T, D, false, false>(a, s);
 }
 
 template <typename T>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 32: return a.causal ? launch_typed<T, 32, true>(a, s) : launch_typed<T, 32, false>(a, s);
-    case 64: return a.causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
-    case 128: return a.causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+    case 32: return launch_mask<T, 32>(a, s);
+    case 64: return launch_mask<T, 64>(a, s);
+    case 128: return launch_mask<T, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -368,7 +433,6 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_keysplit(const FwdArgs& a, hipStream_t stream) {
-  if (a.block_table != nullptr) return hipErrorInvalidValue;  // dense and packed batches only
   switch (a.dtype) {
     case 1: return launch_d<_Float16>(a, stream);
     case 2: return launch_d<__bf16>(a, stream);

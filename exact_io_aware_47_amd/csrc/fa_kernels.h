@@ -89,7 +89,7 @@ struct Fp8FwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // The forward whose two wave groups split each 128-row query tile's keys
-// (16-bit types, dense or packed K/V; used for short grids).
+// (16-bit types; dense, packed or paged K/V; used for short grids).
 hipError_t launch_fwd_keysplit(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 size_t fp8_vt_bytes(int B, int Hkv, int Nk, int d);
