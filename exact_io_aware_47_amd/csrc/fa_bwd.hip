@@ -94,6 +94,10 @@ struct DkvParams {
   int tot_q, tot_k;        // packed batch: total query / key tokens
   float c;      // scale * log2(e)
   float scale;
+  // The same exponent scale for the 16-bit kernel, which flips K's sign for
+  // a negative scale: |c| (2^-100 for a zero scale) and the flip.
+  float c_mag;
+  int neg_k;
 };
 
 // Eight consecutive floats of the LDS stats area starting at float index i.
@@ -373,8 +377,8 @@ void bwd_dkdv16_kernel(DkvParams p) {
   const int kw = k0 + 32 * w;
   const int key = kw + col;
   const int diag = Nk - Nq;
-  const bool neg = p.c < 0.f;
-  const float c = neg ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+  const bool neg = p.neg_k;
+  const float c = p.c_mag;
 
   const size_t kv_slab = kv_row0 * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kv_slab * 2, (uint32_t)Nk * C::kRowBytes);
@@ -930,6 +934,8 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.c = a.scale * kLog2e; p.scale = a.scale;
+  const ExpScale es = exp_scale(p.c);
+  p.c_mag = es.c; p.neg_k = es.neg_q;
   const unsigned grid = (unsigned)((a.Nk + C::kBKV - 1) / C::kBKV) * a.B * a.Hkv;
   if (grid == 0) return hipSuccess;  // a packed batch with no key
   // 16-bit types take the pipelined kernel; float32 (whose fragments leave

@@ -316,6 +316,11 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // --------------------------------------------------------------------------
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// The larger of a and b as IEEE maximum (NaN if either is NaN).  On gfx950
+// this is v_maximum3_f32 on the operands as they are; fmaxf (maxnum) first
+// quiets every operand that might be a signalling NaN with one more max.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max(x, x of the lane 32 places away) in every lane, on the VALU
 // (v_permlane32_swap exchanges the upper half of one operand with the lower
 // half of the other; with both operands x the two results hold x's lower and
@@ -323,7 +328,7 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 __device__ __forceinline__ float max_halves(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(as_float((uint32_t)r[0]), as_float((uint32_t)r[1]));
+  return vmax(as_float((uint32_t)r[0]), as_float((uint32_t)r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);

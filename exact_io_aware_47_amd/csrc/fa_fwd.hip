@@ -86,7 +86,8 @@ struct FwdParams {
   // table [B, max_blocks] and cached tokens per sequence are kernel arguments
   // of their own (restrict-qualified, read through the scalar cache).
   int max_blocks, num_blocks;
-  float c;  // scale * log2(e)
+  float c;    // |scale| * log2(e), or 2^-100 for a zero scale
+  int neg_q;  // the scale is negative: Q's sign is flipped instead
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
@@ -198,7 +199,7 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
   Frag qf[C::kKS];
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ks++) qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
-  if (p.c < 0.f) {
+  if (p.neg_q) {
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ks++) qf[ks] = E::negate(qf[ks]);
   }
@@ -237,10 +238,8 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
   }
   float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
   float l = 0.f;        // this lane's share of the running sum (the other half-wave holds the rest)
-  // The max of c*s over a row is c*max(s) only for c > 0: a negative scale
-  // flips the sign of Q instead (exact), a zero scale becomes a tiny positive
-  // one (every exp2 then rounds to 1, as exp2(0) would).
-  const float c = p.c < 0.f ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+  // c > 0, so the max of c*s over a row is c*max(s).
+  const float c = p.c;
 
   // Does this wave see any key of tile j?
   auto active = [&](int j) __attribute__((always_inline)) { return j < n_tiles && (!CAUSAL || j * C::kBC <= qw + 31 + diag); };
@@ -275,11 +274,11 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
     if constexpr (k16) sched_reads_ahead<2 * C::kPS * C::kDT, C::kPS * C::kDT, 4>();
     // Row sums of this P in float32, still in s until S of the next tile
     // overwrites it; added here because the softmax phase is the busier one.
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
+      for (int r = (mt == 0 ? 4 : 0); r < 16; r++) rs[r & 3] += s[mt][r];
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
   // PV of the last tile and S of this tile in one interleaved sequence (16-bit
@@ -291,11 +290,11 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
     if constexpr (k16) {
     constexpr int N = C::kPS * C::kDT;
     static_assert(N == C::kKS * C::kMT, "PV and S have equal product counts");
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) rs[r & 3] += s[mt][r];
+      for (int r = (mt == 0 ? 4 : 0); r < 16; r++) rs[r & 3] += s[mt][r];
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++) s[mt] = f32x16{};
@@ -334,8 +333,8 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
       for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-          x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
-    const float mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * c;
+          x[i] = r + 4 + i < 16 ? vmax(vmax(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : vmax(x[i], s[mt][r + i]);
+    const float mx = max_halves(vmax(vmax(x[0], x[1]), vmax(x[2], x[3]))) * c;
     // Move the running max only if it grows by more than kTau.
     const bool grow = mx > m + kTau;
     if (__any(grow)) {
@@ -462,7 +461,8 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.max_blocks = a.max_blocks; p.num_blocks = a.num_blocks;
-  p.c = a.scale * kLog2e;
+  const ExpScale es = exp_scale(a.scale * kLog2e);
+  p.c = es.c; p.neg_q = es.neg_q;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;  // a packed batch with no query
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, PAGED, W>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,

@@ -117,7 +117,8 @@ struct Fp8Params {
   void* o;            // bf16 [B, Hq, Nq, D]
   float* lse;
   int B, Hq, Hkv, Nq, Nk, n_ktiles;
-  float c;          // scale * q_descale * k_descale * log2(e)
+  float c;          // |scale * q_descale * k_descale| * log2(e), or 2^-100 for zero
+  int neg_q;        // that product is negative: Q's sign bits are flipped instead
   float v_descale;
 };
 
@@ -181,13 +182,13 @@ void fwd_fp8_kernel(Fp8Params p) {
     const u32x4 a = buf_load16(rq, off), bq = buf_load16(rq, off + 16);
     qf[kb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)bq[0], (int)bq[1], (int)bq[2], (int)bq[3]};
   }
-  // The max of c*s is c*max(s) only for c > 0: a negative scale flips Q's
-  // sign bits instead (exact), a zero scale becomes a tiny positive one.
-  if (p.c < 0.f) {
+  // c > 0, so the max of c*s is c*max(s); a negative scale flips Q's sign
+  // bits instead (exact).
+  if (p.neg_q) {
 #pragma unroll
     for (int kb = 0; kb < C::kKB; kb++) qf[kb] ^= (int)0x80808080;
   }
-  const float c = p.c < 0.f ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+  const float c = p.c;
 
   // Per-lane LDS offsets of the A fragments.
   uint32_t koff[2][C::kKB][2], voff[C::kDT][2];
@@ -235,8 +236,8 @@ void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int r = (mt == 0 ? 4 : 0); r < 16; r += 4)
 #pragma unroll
-        for (int i = 0; i < 4; i++) x[i] = fmaxf(x[i], s[mt][r + i]);
-    const float mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * c;
+        for (int i = 0; i < 4; i++) x[i] = vmax(x[i], s[mt][r + i]);
+    const float mx = max_halves(vmax(vmax(x[0], x[1]), vmax(x[2], x[3]))) * c;
     const bool grow = mx > m + kTauFp8;
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m - mx) : 1.f;
@@ -246,13 +247,13 @@ void fwd_fp8_kernel(Fp8Params p) {
       for (int dt = 0; dt < C::kDT; dt++) o[dt] *= alpha;
     }
     const float m_use = (m == -INFINITY ? 0.f : m) - kPShift;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4];
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         s[mt][r] = fast_exp2(fmaf(s[mt][r], c, -m_use));
-        rs[r & 3] += s[mt][r];
+        rs[r & 3] = (mt == 0 && r < 4) ? s[mt][r] : rs[r & 3] + s[mt][r];
       }
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     // ---- Pᵀ as E4M3 bytes in key order (byte t = key 32h + t).
@@ -316,7 +317,8 @@ hipError_t launch_typed(const Fp8FwdArgs& a, hipStream_t stream) {
   p.q = (const uint8_t*)a.q; p.k = (const uint8_t*)a.k; p.vt = (const uint8_t*)a.workspace;
   p.o = a.o; p.lse = a.lse;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk; p.n_ktiles = n_ktiles;
-  p.c = a.scale * a.q_descale * a.k_descale * kLog2e;
+  const ExpScale es = exp_scale(a.scale * a.q_descale * a.k_descale * kLog2e);
+  p.c = es.c; p.neg_q = es.neg_q;
   p.v_descale = a.v_descale;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p);

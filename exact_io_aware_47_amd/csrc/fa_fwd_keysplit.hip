@@ -70,7 +70,8 @@ struct KsParams {
   // table [B, max_blocks] and cached tokens per sequence are kernel arguments
   // of their own (restrict-qualified, read through the scalar cache).
   int max_blocks, num_blocks;
-  float c;  // scale * log2(e)
+  float c;    // |scale| * log2(e), or 2^-100 for a zero scale
+  int neg_q;  // the scale is negative: Q's sign is flipped instead
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescaling threshold (log2 units)
@@ -199,7 +200,7 @@ void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const 
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) {
     qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
-    if (p.c < 0.f) qf[ks] = E::negate(qf[ks]);
+    if (p.neg_q) qf[ks] = E::negate(qf[ks]);
   }
 
   // Per-lane LDS offsets of the K row fragments (A rows are sigma-permuted
@@ -219,7 +220,7 @@ void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const 
   Frag pf[PS];    // its probabilities, consumed by the next matrix phase
   float m = -INFINITY;  // running (possibly stale) max of scale*log2e*s, log2 domain
   float l = 0.f;        // this lane's share of the running sum
-  const float c = p.c < 0.f ? -p.c : (p.c > 0.f ? p.c : 0x1p-100f);
+  const float c = p.c;  // > 0, so the max of c*s over a row is c*max(s)
 
   // Does this wave see any key of tile j?
   auto active = [&](int j) __attribute__((always_inline)) {
@@ -270,8 +271,8 @@ void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const 
       for (int r = (mt == 0 ? 4 : 0); r < 16; r += 8)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-          x[i] = r + 4 + i < 16 ? fmaxf(fmaxf(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : fmaxf(x[i], s[mt][r + i]);
-    const float mx = max_halves(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) * c;
+          x[i] = r + 4 + i < 16 ? vmax(vmax(x[i], s[mt][r + i]), s[mt][r + 4 + i]) : vmax(x[i], s[mt][r + i]);
+    const float mx = max_halves(vmax(vmax(x[0], x[1]), vmax(x[2], x[3]))) * c;
     // Move the running max only if it grows by more than kTau.
     const bool grow = mx > m + kTau;
     if (__any(grow)) {
@@ -282,13 +283,13 @@ void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const 
       for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
     }
     const float m_use = m == -INFINITY ? 0.f : m;  // rows that have seen no key yet
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         s[mt][r] = fast_exp2(fmaf(s[mt][r], c, -m_use));
-        rs[r & 3] += s[mt][r];
+        rs[r & 3] = (mt == 0 && r < 4) ? s[mt][r] : rs[r & 3] + s[mt][r];
       }
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     // Pᵀ k block ps = registers 8*(ps%2).. of M tile ps/2.
@@ -363,7 +364,7 @@ void fwd_keysplit_kernel(KsParams p, const int* __restrict__ block_table, const 
   if (G == 1) return;
   {
     const float m1 = st[lane], l1 = st[64 + lane];
-    const float M = fmaxf(m, m1);
+    const float M = vmax(m, m1);
     const float a0 = m == -INFINITY ? 0.f : fast_exp2(m - M);
     const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
     l = a0 * l + a1 * l1;
@@ -405,7 +406,8 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t stream) {
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.max_blocks = a.max_blocks; p.num_blocks = a.num_blocks;
-  p.c = a.scale * kLog2e;
+  const ExpScale es = exp_scale(a.scale * kLog2e);
+  p.c = es.c; p.neg_q = es.neg_q;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_keysplit_kernel<T, D, CAUSAL, PAGED>), dim3(grid), dim3(64 * C::kWaves), 0, stream, p,

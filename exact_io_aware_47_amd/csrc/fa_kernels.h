@@ -87,6 +87,18 @@ struct Fp8FwdArgs {
   bool causal;
 };
 
+// The exponent scale c = scale * log2(e) (times the FP8 descales) as the
+// forward kernels take it: its magnitude, with a zero scale replaced by 2^-100
+// (every exponential then rounds to 1, as exp(0) would), and whether it is
+// negative (the kernels then flip the sign of Q, or of K in the dK/dV kernel,
+// which is exact, so that the row max of c*s is c times the max of s).  Worked out on the host so that the
+// kernels keep c in a scalar register.
+struct ExpScale {
+  float c;
+  int neg_q;
+};
+inline ExpScale exp_scale(float c) { return ExpScale{c < 0.f ? -c : (c > 0.f ? c : 0x1p-100f), c < 0.f ? 1 : 0}; }
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // The forward whose two wave groups split each 128-row query tile's keys
 // (16-bit types; dense, packed or paged K/V; used for short grids).
