@@ -386,7 +386,14 @@ void fwd_kernel(FwdParams p, const int* __restrict__ block_table, const int* __r
         // active() is monotone in j for a wave (tile j active implies tile j-1
         // active), so this runs PV(j-1) whenever it is due and S(j) with it.
         if (k16) {
-          if (j == 0 ? active(0) : active(j - 1)) gemm_fused(vbuf(jp ^ 1), kbuf(jp));
+          // The matrix phase runs at raised wave priority, so that its MFMA
+          // and LDS instructions win issue arbitration over the softmax wave
+          // on the same SIMD.
+          if (j == 0 ? active(0) : active(j - 1)) {
+            __builtin_amdgcn_s_setprio(3);
+            gemm_fused(vbuf(jp ^ 1), kbuf(jp));
+            __builtin_amdgcn_s_setprio(0);
+          }
         } else {
           if (j >= 1 && active(j - 1)) gemm_pv(vbuf(jp ^ 1));
           // s is (re)defined on both paths, so the probabilities left in it by
