@@ -4,9 +4,11 @@
 One step is the forward and the backward of exact causal attention on the
 bf16 training/prefill workload B=2, H=16, N=4096, d=128 (seeded synthetic
 N(0,1) inputs, resident in device memory before timing starts).  The
-backward is launched as its three phases (row terms, dK/dV, dQ) so that HIP
-events on the library's stream time every kernel of the step separately;
-the roofline object describes whichever kernel takes the most time.
+backward is launched as the two kernels flash_attn_bwd runs (dQ, which
+also computes the per-row terms, then dK/dV) through their phase entry
+points, so that HIP events on the library's stream time every kernel of the
+step separately; the roofline object describes whichever kernel takes the
+most time.
 
 The same run also times, each reported under its own key: the same step on
 the grouped-query shape (`gqa`), on a packed batch of variable-length
@@ -86,11 +88,6 @@ def visible_pairs(nq: int, nk: int, causal: bool) -> int:
 def attention_flops(B, Hq, nq, nk, d, causal):
     pairs = B * Hq * visible_pairs(nq, nk, causal)
     return {"fwd": 4 * d * pairs, "dkdv": 8 * d * pairs, "dq": 2 * d * pairs}
-
-
-def prep_bytes(B, Hq, nq, d, es):
-    rows = B * Hq * nq
-    return rows * (2 * d * es + 4 + 2 * 4)  # read O, dO, LSE; write D and LSE*log2(e)
 
 
 def decode_bytes(B, Hq, Hkv, seq_len, d, es, block_size=16):
@@ -193,21 +190,22 @@ def bench_training(torch, fa, si, steps, warmup, inputs, name="mha_bf16_4k", cau
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, code), dtype=torch.uint8,
                      device="cuda")
 
+    # The backward as flash_attn_bwd runs it: dQ computing the row terms
+    # (D_i, LSE_i*log2(e)) into the workspace, then dK/dV reading them; one
+    # event between the two so that each kernel is timed on its own.
     def step(ev=None):
         if ev: ev[0].record()
         fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
         if ev: ev[1].record()
-        fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, causal)
+        fa.bwd_phase("dq_rowterms", q, k, v, o, do, lse, dq, None, None, ws, causal)
         if ev: ev[2].record()
         fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, causal)
         if ev: ev[3].record()
-        fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, causal)
-        if ev: ev[4].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -218,7 +216,7 @@ def bench_training(torch, fa, si, steps, warmup, inputs, name="mha_bf16_4k", cau
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    names = ["fwd", "prep", "dkdv", "dq"]
+    names = ["fwd", "dq", "dkdv"]
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     return w, total_ms / steps, per, wall
 
@@ -422,8 +420,8 @@ def profile_once(torch, fa, si, repeats=1):
     for _ in range(repeats):
         o, lse = fa.fwd(q, k, v, causal=True)
         fa.bwd_phase("preprocess", None, None, None, o, do, lse, None, None, None, ws, True)
+        fa.bwd_phase("dq_rowterms", q, k, v, o, do, lse, dq, None, None, ws, True)
         fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, True)
-        fa.bwd_phase("dq", q, k, v, None, do, None, dq, None, None, ws, True)
     torch.cuda.synchronize()
     del q, k, v, do, o, lse, ws, dq, dk, dv
     wd = si.WORKLOADS["decode_gqa_paged"]
@@ -455,9 +453,9 @@ KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_ke
 
 # The benchmark's legs in the order main() runs them, with the kernel
 # dispatches of one step of each (warm-up and timed steps alike).
-LEG_ORDER = (("mha_f32_small (non-causal)", 4), ("mha_f16 (causal)", 4), ("mha_f16 (non-causal)", 4),
-             ("mha_bf16_16k", 4), ("varlen_bf16", 4), ("prefill_paged_bf16", 1), ("mha_fp8_4k", 2),
-             ("decode_gqa_paged", 2), ("gqa_bf16_4k", 4), ("mha_bf16_4k", 4))
+LEG_ORDER = (("mha_f32_small (non-causal)", 3), ("mha_f16 (causal)", 3), ("mha_f16 (non-causal)", 3),
+             ("mha_bf16_16k", 3), ("varlen_bf16", 3), ("prefill_paged_bf16", 1), ("mha_fp8_4k", 2),
+             ("decode_gqa_paged", 2), ("gqa_bf16_4k", 3), ("mha_bf16_4k", 3))
 ATTENTION_KERNEL = ("fwd_kernel", "fwd_keysplit_kernel", "fwd_fp8_kernel", "fp8_vt_kernel", "bwd_prep_kernel",
                     "bwd_dkdv16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel",
                     "decode_reduce_kernel")
@@ -768,10 +766,10 @@ def main(argv=None):
         flc = attention_flops(wc.B, wc.Hq, wc.Nq, wc.Nk, wc.d, causal)
         peak = PEAK_MFMA_F32 if wc.dtype == "f32" else PEAK_MFMA_BF16
         fwd_tf = flc["fwd"] / (per_c["fwd"] * 1e-3) / 1e12
-        bwd_tf = (flc["dkdv"] + flc["dq"]) / ((per_c["prep"] + per_c["dkdv"] + per_c["dq"]) * 1e-3) / 1e12
+        bwd_tf = (flc["dkdv"] + flc["dq"]) / ((per_c["dkdv"] + per_c["dq"]) * 1e-3) / 1e12
         extra["configs"][f"{cname}_{'causal' if causal else 'noncausal'}"] = {
             "shape": f"B={wc.B} H={wc.Hq} N={wc.Nq} d={wc.d} {wc.dtype}" + (f" Q,K x{wc.qk_mult:g}" if wc.qk_mult != 1 else ""),
-            "fwd_us": round(per_c["fwd"] * 1e3, 2), "bwd_us": round((per_c["prep"] + per_c["dkdv"] + per_c["dq"]) * 1e3, 2),
+            "fwd_us": round(per_c["fwd"] * 1e3, 2), "bwd_us": round((per_c["dkdv"] + per_c["dq"]) * 1e3, 2),
             "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2), "peak": peak,
             "fwd_frac": round(fwd_tf / peak, 4), "bwd_frac": round(bwd_tf / peak, 4)}
     # Packed variable-length batch (16 causal sequences of seeded lengths), same step.
@@ -824,8 +822,7 @@ def main(argv=None):
     step_flops = fl["fwd"] + fl["dkdv"] + fl["dq"]
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    work = {"fwd": ("mfma", fl["fwd"]), "prep": ("hbm", prep_bytes(w.B, w.Hq, w.Nq, w.d, 2)),
-            "dkdv": ("mfma", fl["dkdv"]), "dq": ("mfma", fl["dq"])}
+    work = {"fwd": ("mfma", fl["fwd"]), "dkdv": ("mfma", fl["dkdv"]), "dq": ("mfma", fl["dq"])}
 
     def roofline(name, ms):
         bound, amount = work[name]
@@ -849,7 +846,7 @@ def main(argv=None):
         "roofline": roofline(dominant, per[dominant]),
         "kernels": {n: roofline(n, per[n]) for n in per},
         "fwd_tflops": round(fl["fwd"] / (per["fwd"] * 1e-3) / 1e12, 2),
-        "bwd_tflops": round((fl["dkdv"] + fl["dq"]) / ((per["prep"] + per["dkdv"] + per["dq"]) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round((fl["dkdv"] + fl["dq"]) / ((per["dkdv"] + per["dq"]) * 1e-3) / 1e12, 2),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
         "host_wall_s_timed": round(wall, 4),

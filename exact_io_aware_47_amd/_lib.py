@@ -39,6 +39,8 @@ SIGNATURES = {
     "flash_attn_bwd_preprocess": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "flash_attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "flash_attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "flash_attn_bwd_dq_rowterms": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                                        _vp, _sz, _vp]),
     "flash_attn_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "flash_attn_bwd_varlen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "flash_attn_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -195,9 +197,10 @@ def bwd(q, k, v, out, dout, lse, causal: bool = False, scale=None, dq=None, dk=N
 
 
 def bwd_phase(phase: str, q, k, v, out, dout, lse, dq, dk, dv, workspace, causal: bool = False, scale=None):
-    """Run one backward phase ('preprocess', 'dkdv' or 'dq') on torch's current
-    stream; the outputs and the workspace are caller-allocated.  Arguments not
-    used by the phase may be None."""
+    """Run one backward phase ('preprocess', 'dkdv', 'dq', or 'dq_rowterms':
+    dQ computing the row terms into the workspace itself, in place of
+    'preprocess') on torch's current stream; the outputs and the workspace are
+    caller-allocated.  Arguments not used by the phase may be None."""
     given = dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
     for name, t in given.items():
         if t is not None:
@@ -219,6 +222,10 @@ def bwd_phase(phase: str, q, k, v, out, dout, lse, dq, dk, dv, workspace, causal
     elif phase == "dq":
         code = L.flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), B, Hq, Hkv, Nq, Nk, d, sc,
                                    int(bool(causal)), code_dt, *ws, _stream(ref.device))
+    elif phase == "dq_rowterms":
+        code = L.flash_attn_bwd_dq_rowterms(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                                            B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), code_dt, *ws,
+                                            _stream(ref.device))
     else:
         raise ValueError(f"unknown backward phase {phase!r}")
     _check(code, f"flash_attn_bwd_{phase}")

@@ -156,7 +156,7 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
                    int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
   const BwdPtrs t = {Q, K, V, O, dO, LSE, dQ, dK, dV, workspace};
-  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdAll, stream);
+  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdFused, stream);
 }
 
 int flash_attn_bwd_preprocess(const void* O, const void* dO, const float* LSE, int B, int Hq, int Nq, int d,
@@ -180,6 +180,15 @@ int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* d
   if (!Q || !K || !V || !dO || !dQ) return FA_ERR_NULL;
   const BwdPtrs t = {Q, K, V, nullptr, dO, nullptr, dQ, nullptr, nullptr, workspace};
   return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdDq, stream);
+}
+
+int flash_attn_bwd_dq_rowterms(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                               const float* LSE, void* dQ, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                               float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ) return FA_ERR_NULL;
+  const BwdPtrs t = {Q, K, V, O, dO, LSE, dQ, nullptr, nullptr, workspace};
+  return run_bwd(t, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, workspace_bytes, fa::kBwdDqRowTerms, stream);
 }
 
 size_t flash_attn_bwd_varlen_workspace_bytes(int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
@@ -210,7 +219,7 @@ int flash_attn_bwd_varlen(const void* Q, const void* K, const void* V, const voi
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = max_seqlen_q; a.Nk = max_seqlen_k; a.d = d;
   a.scale = scale; a.causal = causal != 0; a.dtype = dtype;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.tot_q = total_q; a.tot_k = total_k;
-  return launch_status(fa::launch_bwd(a, fa::kBwdAll, (hipStream_t)stream));
+  return launch_status(fa::launch_bwd(a, fa::kBwdFused, (hipStream_t)stream));
 }
 
 int flash_attn_prefill_paged(const void* Q, const void* K_cache, const void* V_cache, const int* block_table,

@@ -716,6 +716,13 @@ struct DqParams {
   const float* lse2;
   const float* dsum;
   void* dq;
+  // ROWTERMS: the forward's O and LSE, from which the kernel computes its
+  // rows' D_i and LSE_i*log2(e) and writes them to the workspace (lse2w,
+  // dsumw: the same arrays as lse2, dsum).
+  const void* o;
+  const float* lse;
+  float* lse2w;
+  float* dsumw;
   const int* cu_q;  // packed batch: cumulative query / key counts [B + 1], else null
   const int* cu_k;
   int B, Hq, Hkv, Nq, Nk;  // Nq, Nk: the lengths (dense) or their bounds (packed)
@@ -724,7 +731,10 @@ struct DqParams {
   float scale;
 };
 
-template <typename T, int D, bool CAUSAL>
+// ROWTERMS: the kernel computes its rows' terms D_i = sum_c dO_ic O_ic and
+// LSE_i * log2(e) itself (what the preprocess kernel does) and stores them in
+// the workspace for a dK/dV kernel launched after it.
+template <typename T, int D, bool CAUSAL, bool ROWTERMS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(DqParams p) {
   using C = DqCfg<T, D>;
@@ -789,8 +799,35 @@ void bwd_dq_kernel(DqParams p) {
     qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
     dof[ks] = F::template global_row<D>(rdo, qrow, ks, h);
   }
-  const float l2 = as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)qrow * 4, 0, 0));
-  const float dd = as_float(__builtin_amdgcn_raw_buffer_load_b32(rsd, (uint32_t)qrow * 4, 0, 0));
+  float l2, dd;
+  if constexpr (ROWTERMS) {
+    // This lane holds elements d = 16ks + 8h + 0..7 of its row of dO; the
+    // same elements of O give its half of the row sum, the lane 32 places
+    // away the other half.
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)p.o + q_slab * C::kES, (uint32_t)Nq * C::kRowBytes);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ks++) {
+      const Frag of = F::template global_row<D>(ro, qrow, ks, h);
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        if constexpr (C::kES == 2) part = fmaf((float)dof[ks][t], (float)of[t], part);
+        else part = fmaf(dof[ks].v[t], of.v[t], part);
+      }
+    }
+    dd = sum_halves(part);
+    const float L = as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lse + q_row0, (uint32_t)Nq * 4),
+                                                                  (uint32_t)qrow * 4, 0, 0));
+    // Rows that see no key carry LSE = -inf; +inf makes exp2(s - lse2) vanish.
+    l2 = L == -INFINITY ? INFINITY : L * kLog2e;
+    if (h == 0) {
+      buf_store4(make_rsrc(p.dsumw + q_row0, (uint32_t)Nq * 4), (uint32_t)qrow * 4, __builtin_bit_cast(uint32_t, dd));
+      buf_store4(make_rsrc(p.lse2w + q_row0, (uint32_t)Nq * 4), (uint32_t)qrow * 4, __builtin_bit_cast(uint32_t, l2));
+    }
+  } else {
+    l2 = as_float(__builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)qrow * 4, 0, 0));
+    dd = as_float(__builtin_amdgcn_raw_buffer_load_b32(rsd, (uint32_t)qrow * 4, 0, 0));
+  }
 
   f32x16 dq[C::kDT];
 #pragma unroll
@@ -947,28 +984,35 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool ROWTERMS>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   using C = DqCfg<T, D>;
   const int64_t rows = query_rows(a);
   DqParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.lse2 = a.dsum + rows; p.dsum = a.dsum; p.dq = a.dq;
+  p.o = a.o; p.lse = a.lse; p.lse2w = a.dsum + rows; p.dsumw = a.dsum;
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.tot_q = a.tot_q; p.tot_k = a.tot_k;
   p.c = a.scale * kLog2e; p.scale = a.scale;
   const unsigned grid = (unsigned)((a.Nq + C::kBR - 1) / C::kBR) * a.B * a.Hq;
   if (grid == 0) return hipSuccess;  // a packed batch with no query
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ROWTERMS>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_phases(const BwdArgs& a, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  if (phases & kBwdDqRowTerms) {
+    // dQ with the row terms first, then dK/dV, which reads them.
+    if ((e = launch_dq<T, D, CAUSAL, true>(a, stream)) != hipSuccess) return e;
+    if ((phases & kBwdDkdv) && (e = launch_dkdv<T, D, CAUSAL>(a, stream)) != hipSuccess) return e;
+    return e;
+  }
   if ((phases & kBwdPrep) && (e = launch_prep<T, D>(a, stream)) != hipSuccess) return e;
   if ((phases & kBwdDkdv) && (e = launch_dkdv<T, D, CAUSAL>(a, stream)) != hipSuccess) return e;
-  if ((phases & kBwdDq) && (e = launch_dq<T, D, CAUSAL>(a, stream)) != hipSuccess) return e;
+  if ((phases & kBwdDq) && (e = launch_dq<T, D, CAUSAL, false>(a, stream)) != hipSuccess) return e;
   return e;
 }
 

@@ -106,7 +106,11 @@ hipError_t launch_fwd_keysplit(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 size_t fp8_vt_bytes(int B, int Hkv, int Nk, int d);
 // Backward phases (bit mask); kBwdAll runs them in order on one stream.
-constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
+// kBwdDqRowTerms is the dQ phase computing the row terms itself (in place of
+// kBwdPrep); with kBwdDkdv it runs first and dK/dV after it, and kBwdFused is
+// that pair, the whole backward in two kernels.
+constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7, kBwdDqRowTerms = 8;
+constexpr int kBwdFused = kBwdDqRowTerms | kBwdDkdv;
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -111,7 +111,8 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, in
  * accumulated into).  dK and dV of a K/V head are summed over the query heads
  * of its group.  workspace must hold flash_attn_bwd_workspace_bytes(...)
  * bytes; its contents on entry are ignored.  Deterministic: identical inputs
- * give bitwise identical outputs.
+ * give bitwise identical outputs.  Runs flash_attn_bwd_dq_rowterms, then
+ * flash_attn_bwd_dkdv, on one stream.
  * Errors: as flash_attn_fwd, with FA_ERR_WORKSPACE checked before FA_ERR_ALIGN.
  */
 int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -120,14 +121,19 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
                    int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The backward's three phases, for callers that schedule them themselves
- * (flash_attn_bwd runs all three in this order on one stream):
+ * The backward's phases, for callers that schedule them themselves:
  *   1. flash_attn_bwd_preprocess writes the per-row terms D_i and
  *      LSE_i*log2(e) into the workspace (reads O, dO, LSE);
  *   2. flash_attn_bwd_dkdv writes dK, dV and flash_attn_bwd_dq writes dQ;
  *      both read the workspace written by phase 1 and are independent of
  *      each other, so they may run concurrently on two streams once phase 1
  *      has completed.
+ * flash_attn_bwd_dq_rowterms is phase 2's dQ computing the row terms of its
+ * own rows (it reads O, dO and LSE as well) and writing them into the
+ * workspace, in place of phase 1: flash_attn_bwd_dkdv may run after it has
+ * completed.  flash_attn_bwd runs these two in that order; the row terms are
+ * the same up to float32 rounding order, so its results can differ from the
+ * three-phase order in the last bits.
  * Arguments mean what they mean for flash_attn_bwd; the workspace must hold
  * flash_attn_bwd_workspace_bytes(...) bytes.  Same error codes and order.
  */
@@ -141,6 +147,10 @@ int flash_attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void*
 int flash_attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, void* dQ,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                       int dtype, const void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_bwd_dq_rowterms(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                               const float* LSE, void* dQ,
+                               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                               int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed (variable-length) batches.  Sources: the related-work page

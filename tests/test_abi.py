@@ -70,7 +70,7 @@ def test_header_declares_the_entry_points():
               "flash_attn_bwd_workspace_bytes", "flash_attn_decode_workspace_bytes", "flash_attn_decode_num_splits",
               "flash_attn_fwd_varlen", "flash_attn_bwd_varlen", "flash_attn_bwd_varlen_workspace_bytes",
               "flash_attn_prefill_paged", "flash_attn_fwd_fp8", "flash_attn_fwd_fp8_workspace_bytes",
-              "flash_attn_decode_paged_noalloc"):
+              "flash_attn_decode_paged_noalloc", "flash_attn_bwd_dq_rowterms"):
         assert n in names
 
 
@@ -123,6 +123,19 @@ def bwd(L, ws=P, ws_bytes=1 << 20, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.1
 ])
 def test_bwd_validation(L, kw, code):
     assert bwd(L, **kw) == code
+
+
+def test_bwd_dq_rowterms_validation(L):
+    # Q, K, V, O, dO, LSE, dQ are required; the workspace must hold the row terms.
+    args = [P] * 7
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert L.flash_attn_bwd_dq_rowterms(*a, 2, 2, 2, 8, 8, 64, 0.1, 1, BF16, P, 1 << 20, None) == NULL
+    assert L.flash_attn_bwd_dq_rowterms(*args, 2, 2, 2, 8, 8, 48, 0.1, 1, BF16, P, 1 << 20, None) == HEADDIM
+    assert L.flash_attn_bwd_dq_rowterms(*args, 2, 2, 2, 8, 8, 64, 0.1, 1, BF16, None, 1 << 20, None) == WORKSPACE
+    assert L.flash_attn_bwd_dq_rowterms(*args, 2, 2, 2, 8, 8, 64, 0.1, 1, BF16, P, 2 * 2 * 2 * 8 * 4 - 1,
+                                        None) == WORKSPACE
 
 
 def fwd_vl(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=3, Hq=4, Hkv=2, tq=300, tk=300, mq=200, mk=200, d=128,
@@ -297,6 +310,7 @@ def test_valid_calls_reach_the_launchers(L):
         lambda: L.flash_attn_bwd_preprocess(A, A, A, 1, 4, 100, 64, BF16, A, big, None),
         lambda: L.flash_attn_bwd_dkdv(A, A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
         lambda: L.flash_attn_bwd_dq(A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
+        lambda: L.flash_attn_bwd_dq_rowterms(A, A, A, A, A, A, A, 1, 4, 2, 100, 200, 64, 0.1, 1, BF16, A, big, None),
         lambda: fwd_vl(L, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A),
         lambda: fwd_vl(L, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, tq=0, mq=0, tk=0, mk=0),
         lambda: L.flash_attn_bwd_varlen(A, A, A, A, A, A, A, A, A, A, A, 3, 4, 2, 300, 300, 200, 200, 64, 0.1, 1,

@@ -119,5 +119,6 @@ def test_trace_summary_labels_dispatches_by_leg(tmp_path):
         w.writerows(rows)
     text = bench.trace_summary(str(tmp_path / "trace.csv"), steps, warmup)
     line = [l for l in text.splitlines() if l.startswith("| mha_bf16_4k |")][0]
-    assert "`fwd_kernel<bf16, 128, 1, 0, 8>`" in line and "| 12 | 3.00 | 3.00 |" in line
+    calls = (steps + warmup) * dict(bench.LEG_ORDER)["mha_bf16_4k"]
+    assert "`fwd_kernel<bf16, 128, 1, 0, 8>`" in line and f"| {calls} | 3.00 | 3.00 |" in line
     assert any(l.startswith("| (torch / runtime) |") for l in text.splitlines())

@@ -169,15 +169,24 @@ def test_bwd_bitwise_repeatable():
         assert torch.equal(a, b)
 
 
+def _three_phases(fa, qd, kd, vd, o, dod, lse, ws, causal):
+    """Preprocess, dK/dV, dQ in that order on the current stream."""
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    fa.bwd_phase("preprocess", None, None, None, o, dod, lse, None, None, None, ws, causal)
+    fa.bwd_phase("dkdv", qd, kd, vd, None, dod, None, None, dk, dv, ws, causal)
+    fa.bwd_phase("dq", qd, kd, vd, None, dod, None, dq, None, None, ws, causal)
+    return dq, dk, dv
+
+
 def test_bwd_phases_on_two_streams_match_single_call():
     """Preprocess, then dK/dV on the current stream and dQ on a second stream
-    concurrently: bitwise equal to flash_attn_bwd on one stream."""
+    concurrently: bitwise equal to the three phases in order on one stream."""
     fa = _fa()
     q, k, v, do = si.make_attention_inputs(2, 8, 4, 513, 513, 64, "f16", seed=6)
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     o, lse = fa.fwd(qd, kd, vd, causal=True)
-    ref = fa.bwd(qd, kd, vd, o, dod, lse, causal=True)
     ws = torch.empty(fa.bwd_workspace_bytes(2, 8, 4, 513, 513, 64, fa.FA_F16), dtype=torch.uint8, device="cuda")
+    ref = _three_phases(fa, qd, kd, vd, o, dod, lse, ws, True)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -192,3 +201,52 @@ def test_bwd_phases_on_two_streams_match_single_call():
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), ref):
         assert torch.equal(a, b)
+
+
+# B, Hq, Hkv, Nq, Nk, d, dtype, causal: ragged tails, GQA, more queries than
+# keys (causal rows that see no key), all three element types.
+ROWTERM_CASES = [
+    (2, 8, 4, 513, 513, 64, "f16", True),
+    (1, 4, 2, 700, 256, 128, "bf16", True),
+    (1, 2, 2, 129, 300, 32, "f32", False),
+    (2, 4, 1, 333, 333, 128, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", ROWTERM_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_{c[3]}x{c[4]}_d{c[5]}_{c[6]}_{'c' if c[7] else 'nc'}"
+                              for c in ROWTERM_CASES])
+def test_bwd_is_dq_with_row_terms_then_dkdv(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    """flash_attn_bwd is the dQ phase that computes the row terms followed by
+    dK/dV: bitwise equal to those two phases called in order.  The row terms
+    it leaves in the workspace agree with the preprocess kernel's (LSE*log2(e)
+    bitwise; D_i within the rounding of a float32 sum of d products), and the
+    gradients agree with the three-phase order to the same bound as each has
+    with the oracle, which both are checked against."""
+    fa = _fa()
+    q, k, v, do = si.make_attention_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed=11)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal)
+    fused = fa.bwd(qd, kd, vd, o, dod, lse, causal=causal)
+    code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype]
+    nbytes = fa.bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, code)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    fa.bwd_phase("dq_rowterms", qd, kd, vd, o, dod, lse, dq, None, None, ws, causal)
+    rows = B * Hq * Nq
+    terms = ws[: 8 * rows].view(torch.float32).clone()
+    fa.bwd_phase("dkdv", qd, kd, vd, None, dod, None, None, dk, dv, ws, causal)
+    ws3 = torch.empty_like(ws)
+    three = _three_phases(fa, qd, kd, vd, o, dod, lse, ws3, causal)
+    terms3 = ws3[: 8 * rows].view(torch.float32).clone()
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), fused):
+        assert torch.equal(a, b)
+    assert torch.equal(terms[rows:], terms3[rows:])
+    dsum, dsum3 = terms[:rows].double(), terms3[:rows].double()
+    mag = (dod.double() * o.double()).abs().sum(-1).reshape(-1)
+    assert torch.all((dsum - dsum3).abs() <= 2 * d * 2.0 ** -24 * mag + 1e-30)
+    sc = scale_for(d)
+    rq, rk, rv = orc.attention_bwd(f64(q), f64(k), f64(v), f64(do), sc, causal)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert_close(name, f64(g.cpu()), r, dtype, "grad")
