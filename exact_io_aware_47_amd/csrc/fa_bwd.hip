@@ -810,9 +810,18 @@ void bwd_dq_kernel(DqParams p) {
     for (int ks = 0; ks < C::kKS; ks++) {
       const Frag of = F::template global_row<D>(ro, qrow, ks, h);
 #pragma unroll
-      for (int t = 0; t < 8; t++) {
-        if constexpr (C::kES == 2) part = fmaf((float)dof[ks][t], (float)of[t], part);
-        else part = fmaf(dof[ks].v[t], of.v[t], part);
+      for (int t = 0; t < 8; t += 2) {
+        // 16-bit types: one two-element dot product with float32 accumulation per pair.
+        if constexpr (std::is_same_v<T, __bf16>) {
+          typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+          part = __builtin_amdgcn_fdot2_f32_bf16(v2{dof[ks][t], dof[ks][t + 1]}, v2{of[t], of[t + 1]}, part, false);
+        } else if constexpr (std::is_same_v<T, _Float16>) {
+          typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+          part = __builtin_amdgcn_fdot2(v2{dof[ks][t], dof[ks][t + 1]}, v2{of[t], of[t + 1]}, part, false);
+        } else {
+          part = fmaf(dof[ks].v[t], of.v[t], part);
+          part = fmaf(dof[ks].v[t + 1], of.v[t + 1], part);
+        }
       }
     }
     dd = sum_halves(part);
