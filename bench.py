@@ -408,9 +408,10 @@ def cpu_baseline(si):
 
 
 def profile_once(torch, fa, si, repeats=1):
-    """``repeats`` launches of every kernel of the training step, of the decode
-    and of the FP8 forward, then a 1 GiB device-to-device copy (counter
-    calibration).  Counter readers take the last launch of each kernel (util)
+    """``repeats`` launches of every kernel of the training step (forward, dQ
+    with the row terms, dK/dV; also the separate row-term kernel of the
+    preprocess phase), of the decode and of the FP8 forward, then a 1 GiB
+    device-to-device copy (counter calibration).  Counter readers take the last launch of each kernel (util)
     or the mean over launches (bytes, which do not change between launches)."""
     w = si.WORKLOADS["mha_bf16_4k"]
     q, k, v, do = (t.to("cuda") for t in si.workload_attention_inputs(w))
@@ -576,7 +577,7 @@ def util_from(csv_path, out_dir=None):
 # forward's shape; the decode is HBM-bound).
 COUNTER_ROWS = (("fwd", "fwd (`fwd_kernel<bf16,128,causal>`)", "1.375e11"), ("prep", "prep", "—"),
                 ("dkdv", "dkdv (`bwd_dkdv16_kernel`)", "2.750e11"),
-                ("dq", "dq (`bwd_dq_kernel`)", "0.687e11 (2d; S and dP recomputed)"),
+                ("dq", "dq (`bwd_dq_kernel`, computing the row terms)", "0.687e11 (2d; S and dP recomputed)"),
                 ("decode", "decode (`decode_split_kernel`)", "— (HBM-bound)"),
                 ("fp8", "fp8 (`fwd_fp8_kernel`)", "1.375e11"))
 
