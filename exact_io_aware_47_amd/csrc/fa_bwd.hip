@@ -426,18 +426,30 @@ void bwd_dkdv16_kernel(DkvParams p) {
     load_tile(s / n_diag_d, qt0 + s % n_diag_d, buf, valid);
   };
 
-  if (n_dsteps > 0) load_diag(0, 2, true);
-  if (steps > 0) load_step(0, 0, true);
-  if (steps > 1) load_step(1, 1, true);
-
-  // Kᵀ and Vᵀ as B operands (k = d, column = this lane's key).
+  // Kᵀ and Vᵀ as B operands (k = d, column = this lane's key), loaded before
+  // the first tiles: the first step then waits for these and its own tile
+  // only, while the two pipelined steps' tiles are still in flight.
   Frag kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) {
     kf[ks] = F::template global_row<D>(rk, key, ks, h);
     vf[ks] = F::template global_row<D>(rv, key, ks, h);
-    if (neg) kf[ks] = E::negate(kf[ks]);
   }
+  // The first three tiles' loads are issued whether or not their tiles exist
+  // (an absent one reads an empty range), so that every wave has the same
+  // fixed number of loads in flight behind the K/V fragments.
+  __builtin_amdgcn_sched_barrier(0);
+  load_diag(0, 2, n_dsteps > 0);
+  load_step(0, 0, steps > 0);
+  load_step(1, 1, steps > 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // Vector-memory instructions of one tile load (per wave): Q, dO, stats.
+  using TS = DmaShape<C::kRowBytes, C::kBQ, C::kWaves>;
+  static_assert(TS::kActive == C::kWaves, "every wave issues the same tile loads");
+  constexpr int kTileLoads = 2 * TS::kPer + 1;
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+    if (neg) kf[ks] = E::negate(kf[ks]);
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
@@ -510,9 +522,11 @@ void bwd_dkdv16_kernel(DkvParams p) {
   // ---- Diagonal tiles (causal only), unpipelined, alternating between
   // buffers 2 and 3; each step's barrier publishes its tiles and frees the
   // other buffer for the next tile's loads.
-  auto diag_step = [&](auto bc, int s) __attribute__((always_inline)) {
+  auto diag_step = [&](auto bc, int s, auto fc) __attribute__((always_inline)) {
     constexpr int bi = decltype(bc)::value;
-    wait_vmem();
+    // The first diagonal tile leaves the pipelined steps' loads in flight.
+    if constexpr (decltype(fc)::value) wait_vmem_le<2 * kTileLoads>();
+    else wait_vmem();
     barrier_lds();
     load_diag(s + 1, 5 - bi, s + 1 < n_dsteps);
     gemm_sdp(qbuf(bi), dobuf(bi));
@@ -520,9 +534,12 @@ void bwd_dkdv16_kernel(DkvParams p) {
     p_ds(stbuf(bi), pa, da);
     gemm_dvdk(qbuf(bi), dobuf(bi), pa, da);
   };
-  for (int s = 0; s < n_dsteps; s += 2) {
-    diag_step(Int<2>{}, s);
-    if (s + 1 < n_dsteps) diag_step(Int<3>{}, s + 1);
+  // The first tile runs outside the loop, in straight-line code after the
+  // prologue's loads, so that its partial wait is the only one.
+  if (n_dsteps > 0) diag_step(Int<2>{}, 0, Int<1>{});
+  for (int s = 1; s < n_dsteps; s += 2) {
+    diag_step(Int<3>{}, s, Int<0>{});
+    if (s + 1 < n_dsteps) diag_step(Int<2>{}, s + 1, Int<0>{});
   }
   // Buffer 3 stands for step -1 of the first pipelined step: zero it once
   // every wave is done with the diagonal tiles.
@@ -663,7 +680,8 @@ void bwd_dkdv16_kernel(DkvParams p) {
           dq_);
   };
 
-  wait_vmem();
+  if (n_dsteps == 0) wait_vmem_le<kTileLoads>();
+  else wait_vmem();
   barrier_lds();
   if (steps > 0) gemm_sdp(qbuf(0), dobuf(0));
   // steps + 1 iterations: the last one only completes dV/dK of the last step.
