@@ -3,12 +3,14 @@
 
 One step is the forward and the backward of exact causal attention on the
 bf16 training/prefill workload B=2, H=16, N=4096, d=128 (seeded synthetic
-N(0,1) inputs, resident in device memory before timing starts).  The
-backward is launched as the two kernels flash_attn_bwd runs (dQ, which
-also computes the per-row terms, then dK/dV) through their phase entry
-points, so that HIP events on the library's stream time every kernel of the
-step separately; the roofline object describes whichever kernel takes the
-most time.
+N(0,1) inputs, resident in device memory before timing starts), through
+the public calls flash_attn_fwd and flash_attn_bwd; the timed region holds
+exactly the K steps and no other event.  Then K more steps run the same
+kernels through the phase entry points (forward; dQ, which also computes
+the per-row terms; dK/dV) with a HIP event between each two on the
+library's stream: they time every kernel separately (each event adds a few
+microseconds between kernels, so these steps do not give the step time).
+The roofline object describes whichever kernel takes the most time.
 
 The same run also times, each reported under its own key: the same step on
 the grouped-query shape (`gqa`), on a packed batch of variable-length
@@ -190,32 +192,43 @@ def bench_training(torch, fa, si, steps, warmup, inputs, name="mha_bf16_4k", cau
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, code), dtype=torch.uint8,
                      device="cuda")
 
-    # The backward as flash_attn_bwd runs it: dQ computing the row terms
-    # (D_i, LSE_i*log2(e)) into the workspace, then dK/dV reading them; one
-    # event between the two so that each kernel is timed on its own.
-    def step(ev=None):
-        if ev: ev[0].record()
+    # One step through the public calls: flash_attn_fwd, then flash_attn_bwd
+    # (dQ computing the row terms D_i and LSE_i*log2(e) into the workspace,
+    # then dK/dV reading them).
+    def step():
         fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        if ev: ev[1].record()
+        fa.bwd(q, k, v, o, do, lse, causal=causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    # The same kernels through the phase entry points, with an event between
+    # each two so that every kernel is timed on its own.  Each event costs the
+    # stream a few microseconds between kernels, so these steps give the
+    # per-kernel times, not the step time.
+    def step_split(ev):
+        ev[0].record()
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        ev[1].record()
         fa.bwd_phase("dq_rowterms", q, k, v, o, do, lse, dq, None, None, ws, causal)
-        if ev: ev[2].record()
+        ev[2].record()
         fa.bwd_phase("dkdv", q, k, v, None, do, None, None, dk, dv, ws, causal)
-        if ev: ev[3].record()
+        ev[3].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        step()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step_split(evs[i])
+    torch.cuda.synchronize()
     names = ["fwd", "dq", "dkdv"]
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     return w, total_ms / steps, per, wall
@@ -223,8 +236,10 @@ def bench_training(torch, fa, si, steps, warmup, inputs, name="mha_bf16_4k", cau
 
 def bench_varlen(torch, fa, si, steps, warmup, inputs):
     """Forward + backward of the packed variable-length workload; the backward
-    runs as one flash_attn_bwd_varlen call.  Returns (workload, lengths,
-    ms per step, {fwd, bwd: ms})."""
+    runs as one flash_attn_bwd_varlen call.  The step time comes from steps
+    with no event inside them, the forward and backward times from as many
+    more steps with an event between the two calls.  Returns (workload,
+    lengths, ms per step, {fwd, bwd: ms})."""
     w = si.WORKLOADS["varlen_bf16"]
     q, k, v, do, cu_q, cu_k = inputs["varlen_bf16"]
     lens = (cu_q[1:] - cu_q[:-1]).tolist()
@@ -247,12 +262,18 @@ def bench_varlen(torch, fa, si, steps, warmup, inputs):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(("fwd", "bwd"))}
-    return w, lens, per["fwd"] + per["bwd"], per
+    return w, lens, t0.elapsed_time(t1) / steps, per
 
 
 def bench_prefill(torch, fa, si, steps, warmup, inputs):
@@ -454,9 +475,14 @@ KERNEL_KEYS = (("fwd_kernel", "fwd"), ("bwd_prep_kernel", "prep"), ("bwd_dkdv_ke
 
 # The benchmark's legs in the order main() runs them, with the kernel
 # dispatches of one step of each (warm-up and timed steps alike).
+# The training legs (fwd + bwd) run their timed steps twice: once through the
+# public calls for the step time, then through the phase entry points with
+# events between the kernels for the per-kernel times.
 LEG_ORDER = (("mha_f32_small (non-causal)", 3), ("mha_f16 (causal)", 3), ("mha_f16 (non-causal)", 3),
              ("mha_bf16_16k", 3), ("varlen_bf16", 3), ("prefill_paged_bf16", 1), ("mha_fp8_4k", 2),
              ("decode_gqa_paged", 2), ("gqa_bf16_4k", 3), ("mha_bf16_4k", 3))
+TWO_PASS_LEGS = ("mha_f32_small (non-causal)", "mha_f16 (causal)", "mha_f16 (non-causal)", "mha_bf16_16k",
+                 "varlen_bf16", "gqa_bf16_4k", "mha_bf16_4k")
 ATTENTION_KERNEL = ("fwd_kernel", "fwd_keysplit_kernel", "fwd_fp8_kernel", "fp8_vt_kernel", "bwd_prep_kernel",
                     "bwd_dkdv16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel",
                     "decode_reduce_kernel")
@@ -479,13 +505,14 @@ def _short_kernel_name(n):
 def trace_summary(trace_csv, steps, warmup):
     """Markdown table of a rocprofv3 kernel trace of one default benchmark
     run: every attention dispatch labelled with its leg (legs run in
-    LEG_ORDER, each with warmup + steps steps), per (leg, kernel) the call
-    count, the average over all calls and over the timed (last `steps`)
-    calls, min, max and total."""
+    LEG_ORDER, each with warmup + steps steps, the training legs with
+    another `steps` steps for their per-kernel times), per (leg, kernel) the
+    call count, the average over all calls and over the last `steps` calls
+    (the ones the per-kernel events cover), min, max and total."""
     import collections
     import csv
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
-    legs = [(n, k * (warmup + steps)) for n, k in LEG_ORDER]
+    legs = [(n, k * (warmup + steps * (2 if n in TWO_PASS_LEGS else 1))) for n, k in LEG_ORDER]
     leg_i, used = 0, 0
     g = collections.defaultdict(list)
     for r in rows:

@@ -109,7 +109,8 @@ def test_trace_summary_labels_dispatches_by_leg(tmp_path):
     names = {"fwd": "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELb1ELb0ELi8EEEvNS0_9FwdParamsEPKiS4_",
              "other": "at::native::elementwise_kernel"}
     for leg, per_step in bench.LEG_ORDER:
-        for _ in range((steps + warmup) * per_step):
+        passes = 2 if leg in bench.TWO_PASS_LEGS else 1
+        for _ in range((steps * passes + warmup) * per_step):
             rows.append((names["fwd"], t, t + 1000 if leg != "mha_bf16_4k" else t + 3000))
             t += 5000
     rows.append((names["other"], t, t + 500))
@@ -119,6 +120,6 @@ def test_trace_summary_labels_dispatches_by_leg(tmp_path):
         w.writerows(rows)
     text = bench.trace_summary(str(tmp_path / "trace.csv"), steps, warmup)
     line = [l for l in text.splitlines() if l.startswith("| mha_bf16_4k |")][0]
-    calls = (steps + warmup) * dict(bench.LEG_ORDER)["mha_bf16_4k"]
+    calls = (2 * steps + warmup) * dict(bench.LEG_ORDER)["mha_bf16_4k"]
     assert "`fwd_kernel<bf16, 128, 1, 0, 8>`" in line and f"| {calls} | 3.00 | 3.00 |" in line
     assert any(l.startswith("| (torch / runtime) |") for l in text.splitlines())
