@@ -12,7 +12,9 @@
 //   dQ = scale dS K,   dK = scale dSᵀ Q
 //
 // Three kernels, all deterministic (no atomics):
-//   bwd_prep : D_i and LSE_i*log2(e) per query row (a streaming pass);
+//   bwd_prep : -D_i and LSE_i*log2(e) per query row (a streaming pass; D is
+//              kept negated so that the dK/dV kernel can start its dP
+//              accumulators from it and get dP - D out of the products);
 //   bwd_dkdv : KV-outer.  A work-group keeps 128 keys (32 per wave) and their
 //              K, V rows in registers and walks every query tile (of every
 //              query head of its group) that can see them.  S = Q Kᵀ is
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, 
 #pragma unroll
   for (int off = kTPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && c == 0) {
-    dsum[row] = acc;
+    dsum[row] = -acc;  // stored negated: the kernels add it (or start dP's accumulator from it)
     const float L = lse[row];
     // Rows that see no key carry LSE = -inf; +inf makes exp2(s - lse2) vanish.
     lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
@@ -251,7 +253,7 @@ void bwd_dkdv_kernel(DkvParams p) {
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] - dd[mt][r >> 3][r & 7]);
+      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] + dd[mt][r >> 3][r & 7]);  // dd = -D
     // ---- dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (column = key, k = query).
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
@@ -469,10 +471,28 @@ void bwd_dkdv16_kernel(DkvParams p) {
 #pragma unroll
   for (int ps = 0; ps < PS; ps++) { pa[ps] = Frag{}; da[ps] = Frag{}; pb[ps] = Frag{}; db[ps] = Frag{}; }
 
-  // S = Q Kᵀ and dP = dO Vᵀ of one step (A rows: sigma-permuted queries).
-  auto gemm_sdp = [&](const lds_char* qb, const lds_char* dob) __attribute__((always_inline)) {
+  // -D of the rows of M tile mt of a step, in the layout of its dP
+  // accumulator (register r: query 32*mt + 16*(r/8) + 8h + (r%8)).
+  auto neg_d = [&](const lds_char* stb, int mt) __attribute__((always_inline)) {
+    float lo[8], hi[8];
+    lds_read8f(stb, C::kBQ + 32 * mt + 8 * h, lo);
+    lds_read8f(stb, C::kBQ + 32 * mt + 16 + 8 * h, hi);
+    f32x16 r;
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+    for (int t = 0; t < 8; t++) { r[t] = lo[t]; r[8 + t] = hi[t]; }
+    return r;
+  };
+  // S = Q Kᵀ and dP = dO Vᵀ of one step (A rows: sigma-permuted queries).
+  // With NEG the dP accumulators start from -D, so that they end as dP - D.
+  auto gemm_sdp = [&](const lds_char* qb, const lds_char* dob, const lds_char* stb, auto negc)
+      __attribute__((always_inline)) {
+    constexpr bool NEG = decltype(negc)::value;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      sv[mt] = f32x16{};
+      if constexpr (NEG) dp[mt] = neg_d(stb, mt);
+      else dp[mt] = f32x16{};
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
 #pragma unroll
@@ -495,13 +515,12 @@ void bwd_dkdv16_kernel(DkvParams p) {
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        float l2[8], dd[8], pv[8], dsv[8];
+        float l2[8], pv[8], dsv[8];
         lds_read8f(stb, 32 * mt + 16 * u + 8 * h, l2);
-        lds_read8f(stb, C::kBQ + 32 * mt + 16 * u + 8 * h, dd);
 #pragma unroll
         for (int t = 0; t < 8; t++) {
           pv[t] = fast_exp2(fmaf(sv[mt][8 * u + t], c, -l2[t]));
-          dsv[t] = pv[t] * (dp[mt][8 * u + t] - dd[t]);
+          dsv[t] = pv[t] * dp[mt][8 * u + t];
         }
         pn[2 * mt + u] = E::pack(pv);
         dn[2 * mt + u] = E::pack(dsv);
@@ -529,7 +548,7 @@ void bwd_dkdv16_kernel(DkvParams p) {
     else wait_vmem();
     barrier_lds();
     load_diag(s + 1, 5 - bi, s + 1 < n_dsteps);
-    gemm_sdp(qbuf(bi), dobuf(bi));
+    gemm_sdp(qbuf(bi), dobuf(bi), stbuf(bi), Int<1>{});
     mask((qt0 + s % n_diag_d) * C::kBQ);
     p_ds(stbuf(bi), pa, da);
     gemm_dvdk(qbuf(bi), dobuf(bi), pa, da);
@@ -563,11 +582,22 @@ void bwd_dkdv16_kernel(DkvParams p) {
   constexpr int kNChunks = NM / kChunk;
   constexpr int kPieces = 2 * MT;
   constexpr int kChunkMt1 = (NA + 2 * KS * (MT - 1)) / kChunk;  // first chunk of the last M tile's S/dP
-  constexpr auto stage_chunk = [](int g) constexpr { return g * kChunkMt1 / (3 * kPieces); };
+  // kNegInit (head size 128): the dP accumulators of the next step start
+  // from -D, loaded in the chunk after the last stage that reads M tile mt's
+  // dP (init_chunk), so that dS = P dP takes one product instead of a
+  // subtraction and a product; the stages then end two chunks earlier to
+  // leave the loads time before the first dP product of the last M tile.
+  // Smaller heads have too few chunks and subtract D in stage 1.
+  constexpr bool kNegInit = kChunkMt1 >= 4 * MT;
+  constexpr int kStageEnd = kNegInit ? kChunkMt1 - 2 : kChunkMt1;
+  constexpr auto stage_chunk = [](int g) constexpr { return g * kStageEnd / (3 * kPieces); };
+  constexpr auto init_chunk = [](int mt) constexpr { return (3 * (2 * mt + 1) + 2) * kStageEnd / (3 * kPieces) + 1; };
+  static_assert(!kNegInit || (init_chunk(0) < (NA + 1) / kChunk && init_chunk(MT - 1) < kChunkMt1),
+                "-D lands in dP before its first product");
 
-  auto fused = [&](const lds_char* stb, const lds_char* q_old, const lds_char* do_old, const lds_char* q_new,
-                   const lds_char* do_new, Frag (&pn)[PS], Frag (&dn)[PS], const Frag (&po)[PS],
-                   const Frag (&dq_)[PS]) __attribute__((always_inline)) {
+  auto fused = [&](const lds_char* stb, const lds_char* stn, const lds_char* q_old, const lds_char* do_old,
+                   const lds_char* q_new, const lds_char* do_new, Frag (&pn)[PS], Frag (&dn)[PS],
+                   const Frag (&po)[PS], const Frag (&dq_)[PS]) __attribute__((always_inline)) {
     float l2[kPieces][8], dd[kPieces][8], pv[kPieces][8], xv[kPieces][8];
     auto read_a = [&](auto mc) __attribute__((always_inline)) -> Frag {
       constexpr int m = decltype(mc)::value;
@@ -588,23 +618,29 @@ void bwd_dkdv16_kernel(DkvParams p) {
       } else {
         constexpr int j = m - NA, mt = j / (2 * KS), ks = (j % (2 * KS)) / 2, which = j % 2;
         if constexpr (which == 0) sv[mt] = E::mma(a, kf[ks], ks == 0 ? f32x16{} : sv[mt]);
-        else dp[mt] = E::mma(a, vf[ks], ks == 0 ? f32x16{} : dp[mt]);
+        else dp[mt] = E::mma(a, vf[ks], (ks == 0 && !kNegInit) ? f32x16{} : dp[mt]);
       }
     };
     auto stats = [&](int pc) __attribute__((always_inline)) {
       const lds_char* sb = stb + 4 * (32 * (pc / 2) + 16 * (pc % 2));
       const u32x4 a0 = lds_read16(sb, soff), a1 = lds_read16(sb + 16, soff);
-      const u32x4 b0 = lds_read16(sb + 4 * C::kBQ, soff), b1 = lds_read16(sb + 4 * C::kBQ + 16, soff);
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         l2[pc][t] = as_float(a0[t]);
         l2[pc][4 + t] = as_float(a1[t]);
-        dd[pc][t] = as_float(b0[t]);
-        dd[pc][4 + t] = as_float(b1[t]);
+      }
+      if constexpr (!kNegInit) {
+        const u32x4 b0 = lds_read16(sb + 4 * C::kBQ, soff), b1 = lds_read16(sb + 4 * C::kBQ + 16, soff);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          dd[pc][t] = as_float(b0[t]);  // -D
+          dd[pc][4 + t] = as_float(b1[t]);
+        }
       }
     };
-    // Stage 0: c s - lse2; stage 1: P = exp2(.), dP - D; stage 2: dS, both
-    // packed, and the next piece's stats read.
+    // Stage 0: c s - lse2; stage 1: P = exp2(.) (and dP - D without
+    // kNegInit); stage 2: dS = P (dP - D), both packed, and the next piece's
+    // stats read.
     auto stage = [&](auto gc) __attribute__((always_inline)) {
       constexpr int gi = decltype(gc)::value, pc = gi / 3, st = gi % 3, mt = pc / 2, u = pc % 2;
       if constexpr (st == 0) {
@@ -614,11 +650,11 @@ void bwd_dkdv16_kernel(DkvParams p) {
 #pragma unroll
         for (int t = 0; t < 8; t++) {
           pv[pc][t] = fast_exp2(xv[pc][t]);
-          xv[pc][t] = dp[mt][8 * u + t] - dd[pc][t];
+          if constexpr (!kNegInit) xv[pc][t] = dp[mt][8 * u + t] + dd[pc][t];
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 8; t++) xv[pc][t] *= pv[pc][t];
+        for (int t = 0; t < 8; t++) xv[pc][t] = (kNegInit ? dp[mt][8 * u + t] : xv[pc][t]) * pv[pc][t];
         pn[pc] = E::pack(pv[pc]);
         dn[pc] = E::pack(xv[pc]);
         if constexpr (pc + 1 < kPieces) stats(pc + 1);
@@ -639,6 +675,12 @@ void bwd_dkdv16_kernel(DkvParams p) {
       static_for<0, 3 * kPieces>([&](auto gc) __attribute__((always_inline)) {
         if constexpr (stage_chunk(decltype(gc)::value) == k) stage(gc);
       });
+      if constexpr (kNegInit) {
+        static_for<0, MT>([&](auto mc) __attribute__((always_inline)) {
+          constexpr int mt = decltype(mc)::value;
+          if constexpr (init_chunk(mt) == k) dp[mt] = neg_d(stn, mt);
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -676,14 +718,14 @@ void bwd_dkdv16_kernel(DkvParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Past the last step S/dP read a stale buffer and P/dS are never used.
-    fused(stbuf(bi), qbuf((bi + 3) & 3), dobuf((bi + 3) & 3), qbuf((bi + 1) & 3), dobuf((bi + 1) & 3), pn, dn, po,
-          dq_);
+    fused(stbuf(bi), stbuf((bi + 1) & 3), qbuf((bi + 3) & 3), dobuf((bi + 3) & 3), qbuf((bi + 1) & 3),
+          dobuf((bi + 1) & 3), pn, dn, po, dq_);
   };
 
   if (n_dsteps == 0) wait_vmem_le<kTileLoads>();
   else wait_vmem();
   barrier_lds();
-  if (steps > 0) gemm_sdp(qbuf(0), dobuf(0));
+  if (steps > 0) gemm_sdp(qbuf(0), dobuf(0), stbuf(0), Int<kNegInit>{});
   // steps + 1 iterations: the last one only completes dV/dK of the last step.
   int i = 0;
   for (; i + 4 <= steps + 1; i += 4) {
@@ -817,7 +859,7 @@ void bwd_dq_kernel(DqParams p) {
     qf[ks] = F::template global_row<D>(rq, qrow, ks, h);
     dof[ks] = F::template global_row<D>(rdo, qrow, ks, h);
   }
-  float l2, dd;
+  float l2, dd;  // LSE_i * log2(e) and -D_i of this lane's row
   if constexpr (ROWTERMS) {
     // This lane holds elements d = 16ks + 8h + 0..7 of its row of dO; the
     // same elements of O give its half of the row sum, the lane 32 places
@@ -842,7 +884,7 @@ void bwd_dq_kernel(DqParams p) {
         }
       }
     }
-    dd = sum_halves(part);
+    dd = -sum_halves(part);  // the workspace holds -D
     const float L = as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lse + q_row0, (uint32_t)Nq * 4),
                                                                   (uint32_t)qrow * 4, 0, 0));
     // Rows that see no key carry LSE = -inf; +inf makes exp2(s - lse2) vanish.
@@ -914,7 +956,7 @@ void bwd_dq_kernel(DqParams p) {
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] - dd);
+      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] + dd);
     // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {

@@ -49,7 +49,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace: D_i = sum_c dO_ic O_ic (one per query row), then LSE_i*log2(e)
+  float* dsum;  // workspace: -D_i = -sum_c dO_ic O_ic (one per query row), then LSE_i*log2(e)
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   bool causal;

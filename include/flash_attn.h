@@ -100,8 +100,8 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
 
 /*
  * Bytes of device workspace flash_attn_bwd needs: two float32 values per query
- * row (the row term D_i = sum_c dO_ic * O_ic and LSE_i * log2(e)).  Returns 0
- * for invalid sizes.
+ * row (the row term D_i = sum_c dO_ic * O_ic, stored negated, and
+ * LSE_i * log2(e)).  Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype);
 
