@@ -920,8 +920,14 @@ void bwd_dq_kernel(DqParams p) {
     if (CAUSAL && k0 > qw + 31 + diag) return;
     // ---- Sᵀ = K Qᵀ and dPᵀ = V dOᵀ; A rows are sigma-permuted keys.
     f32x16 sv[C::kMT], dp[C::kMT];
+    // dPᵀ starts from -D (the same for every register of a lane: its query
+    // row), so the products leave dPᵀ - D.
 #pragma unroll
-    for (int mt = 0; mt < C::kMT; mt++) { sv[mt] = f32x16{}; dp[mt] = f32x16{}; }
+    for (int mt = 0; mt < C::kMT; mt++) {
+      sv[mt] = f32x16{};
+#pragma unroll
+      for (int r = 0; r < 16; r++) dp[mt][r] = dd;
+    }
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ks++) {
 #pragma unroll
@@ -956,7 +962,7 @@ void bwd_dq_kernel(DqParams p) {
 #pragma unroll
     for (int mt = 0; mt < C::kMT; mt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * (dp[mt][r] + dd);
+      for (int r = 0; r < 16; r++) dp[mt][r] = sv[mt][r] * dp[mt][r];
     // ---- dQᵀ += Kᵀ dSᵀ (column = query, k = key).
 #pragma unroll
     for (int ps = 0; ps < C::kPS; ps++) {
