@@ -100,9 +100,14 @@ __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
+// Work-groups of 4 waves (128 query rows, 32 per wave): at head size 128 a
+// wave takes 156 registers, so three work-groups share a compute unit (three
+// waves per SIMD, each from its own work-group and out of step with the
+// others); an 8-wave work-group puts two waves on each SIMD and leaves no
+// room for a second one.
 template <int D>
 struct Fp8Cfg {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = 4;
   static constexpr int kBR = 32 * kWaves;  // query rows per work-group
   static constexpr int kBC = kVtKeys;      // keys per tile
   static constexpr int kKB = D / 64;       // 64-wide k blocks of Sᵀ along d
@@ -132,7 +137,7 @@ __device__ __forceinline__ int pi_row(int i, int mt) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_fp8_kernel(Fp8Params p) {
   using C = Fp8Cfg<D>;
   using TK = Tile<D>;        // K tile: 64 rows of D bytes
