@@ -104,11 +104,13 @@ def test_prefill_equals_dense_forward_bitwise():
         assert torch.equal(o, po) and torch.equal(lse, pl)
 
 
-def test_prefill_and_dense_forward_on_a_short_grid():
-    """A short grid (the key-split kernel for both): the paged call gives
-    bitwise the dense forward's O and LSE, and both match the oracle."""
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_and_dense_forward_on_a_short_grid(d):
+    """A short grid (a key-split kernel for both: at d=64 the causal call runs
+    the 4-wave one): the paged call gives bitwise the dense forward's O and
+    LSE, and both match the oracle."""
     fa = _fa()
-    B, Hq, Hkv, N, d = 2, 4, 2, 333, 128
+    B, Hq, Hkv, N = 2, 4, 2, 333
     q, k, v, _ = si.make_attention_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=93)
     kc, vc, table = _scatter_into_pages(k, v, B, Hkv, N, d, 94)
     lens = torch.full((B,), N, dtype=torch.int32)
