@@ -483,7 +483,8 @@ LEG_ORDER = (("mha_f32_small (non-causal)", 3), ("mha_f16 (causal)", 3), ("mha_f
              ("decode_gqa_paged", 2), ("gqa_bf16_4k", 3), ("mha_bf16_4k", 3))
 TWO_PASS_LEGS = ("mha_f32_small (non-causal)", "mha_f16 (causal)", "mha_f16 (non-causal)", "mha_bf16_16k",
                  "varlen_bf16", "gqa_bf16_4k", "mha_bf16_4k")
-ATTENTION_KERNEL = ("fwd_kernel", "fwd_keysplit_kernel", "fwd_fp8_kernel", "fp8_vt_kernel", "bwd_prep_kernel",
+ATTENTION_KERNEL = ("fwd_kernel", "fwd_keysplit_kernel", "fwd_keysplit_plain_kernel", "fwd_fp8_kernel",
+                    "fp8_vt_kernel", "bwd_prep_kernel",
                     "bwd_dkdv16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel",
                     "decode_reduce_kernel")
 
