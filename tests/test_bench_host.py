@@ -123,3 +123,23 @@ def test_trace_summary_labels_dispatches_by_leg(tmp_path):
     calls = (2 * steps + warmup) * dict(bench.LEG_ORDER)["mha_bf16_4k"]
     assert "`fwd_kernel<bf16, 128, 1, 0, 8>`" in line and f"| {calls} | 3.00 | 3.00 |" in line
     assert any(l.startswith("| (torch / runtime) |") for l in text.splitlines())
+
+
+def test_trace_summary_knows_every_library_kernel():
+    """Every __global__ kernel in the library's HIP sources is one that the
+    trace summary counts as an attention dispatch (a kernel it did not know
+    would be filed under torch / runtime and shift every later leg)."""
+    import glob
+    import re
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "exact_io_aware_47_amd", "csrc")
+    names = set()
+    for path in glob.glob(os.path.join(csrc, "*.hip")):
+        text = open(path).read()
+        for m in re.finditer(r"__global__", text):
+            k = re.search(r"\b(\w+_kernel)\s*\(", text[m.end():m.end() + 400])
+            assert k, f"no kernel name after __global__ in {path}"
+            names.add(k.group(1))
+    assert {"fwd_kernel", "bwd_dkdv16_kernel", "bwd_dq_kernel", "decode_split_kernel"} <= names
+    for n in sorted(names):
+        mangled = f"_ZN2fa12_GLOBAL__N_1{len(n)}{n}IDF16bLi128EEEvv"
+        assert any(k in mangled for k in bench.ATTENTION_KERNEL), n
