@@ -6,7 +6,9 @@
 // concept page "Flash-Attention", "Core idea"), combined with the split of
 // the key sequence that the tutorial's "Variant family" section describes for
 // FlashDecoding: partial softmax results over disjoint key ranges, merged
-// with the correction formula.
+// with the correction formula.  Two kernels: fwd_keysplit_kernel (8 waves,
+// slot schedule) below, and fwd_keysplit_plain_kernel (4 waves, no slot
+// schedule, causal calls with head sizes up to 64) further down.
 //
 // Work decomposition.  A work-group of 8 waves owns kBR = 4 * RW query rows
 // of one (batch, query head).  Waves w and w + 4 (the same SIMD) own the same
